@@ -1,0 +1,169 @@
+"""The FP4 KV cache as a stream of chunk steps, in the library's layout.
+
+TEST INFRASTRUCTURE (CPU oracle); see oracle/__init__.py.
+
+Chains the oracle's parts into the three operations of the path:
+  * append: quantize a new chunk's K and V to NVFP4 and write them in place
+    into the ring of sink + window slots ("in-place quantized KV-cache
+    updates", hysenlabs.com, "NVFP4, sequence parallel and the async decode
+    path");
+  * rope: rotate queries (or keys) by cache-relative position (refft.com,
+    relative RoPE and TriAttention question);
+  * attention: decode the cache and attend with block-causal, window and
+    shot masks (evermx.com, "Multi-Shot Generation").
+
+Cache layout (the byte layout the GPU library must reproduce bit for bit):
+  k_codes, v_codes   uint8 [H][S+W][Tc][D/2]   two E2M1 codes per byte
+  k_scales, v_scales uint8 [H][S+W][Tc][D/16]  E4M3 block-scale codes
+  k_tscale, v_tscale float32 [S+W]             tensor scale g of the frame
+  slot_frame         int32 [S+W]               frame held, -1 when empty
+  slot_shot          int32 [S+W]               shot id of that frame
+The cache holds keys before rotation; keys are rotated after decoding with
+the positions of the current step, so codes are written once and never
+re-quantized when the window slides (reading of "KV-cache relative RoPE").
+
+Keeping every token_stride-th token of each cached frame stands in for the
+pages' KV compression (refft.com, "TriAttention compression"); queries are
+never decimated.  The per-tensor scale is computed over the kept tokens of
+one appended tensor (K or V of one call, all heads).
+"""
+from __future__ import annotations
+
+import copy
+
+import numpy as np
+
+from . import attention as att
+from . import nvfp4
+from . import ring
+from . import rope
+
+
+class OracleCache:
+    def __init__(self, H, D, T, C, S, W, token_stride=1, rot_dim=None,
+                 base=10000.0):
+        assert T % token_stride == 0 and D % nvfp4.BLOCK == 0
+        self.H, self.D, self.T, self.C, self.S, self.W = H, D, T, C, S, W
+        self.stride = token_stride
+        self.Tc = T // token_stride
+        self.rot_dim = D if rot_dim is None else rot_dim
+        self.base = base
+        n = S + W
+        self.k_codes = np.zeros((H, n, self.Tc, D // 2), np.uint8)
+        self.v_codes = np.zeros((H, n, self.Tc, D // 2), np.uint8)
+        self.k_scales = np.zeros((H, n, self.Tc, D // 16), np.uint8)
+        self.v_scales = np.zeros((H, n, self.Tc, D // 16), np.uint8)
+        self.k_tscale = np.ones(n, np.float32)
+        self.v_tscale = np.ones(n, np.float32)
+        self.slot_frame = np.full(n, -1, np.int32)
+        self.slot_shot = np.zeros(n, np.int32)
+
+    @classmethod
+    def for_workload(cls, w, rot_dim=None):
+        return cls(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride, rot_dim)
+
+    def snapshot(self):
+        return copy.deepcopy(self)
+
+    # ---------------------------------------------------------------- append
+    def kept(self, x, n_frames):
+        """[n_frames*T][H][D] -> kept tokens [n_frames][Tc][H][D]."""
+        x = np.asarray(x, dtype=np.float32).reshape(n_frames, self.T, self.H, self.D)
+        return x[:, ::self.stride]
+
+    def append(self, k, v, frame0, n_frames, shots, tscale=None):
+        """Quantize K, V ([n_frames*T][H][D], float32 values) into the slots of
+        frames frame0 .. frame0+n_frames-1.  Returns (g_k, g_v)."""
+        gs = []
+        for idx, (x, codes, scales, tsc) in enumerate((
+                (k, self.k_codes, self.k_scales, self.k_tscale),
+                (v, self.v_codes, self.v_scales, self.v_tscale))):
+            xk = self.kept(x, n_frames)
+            g = nvfp4.tensor_scale(xk) if tscale is None else np.float32(tscale[idx])
+            c, s8 = nvfp4.encode_blocks(xk, g)
+            packed = nvfp4.pack_nibbles(c)
+            for j in range(n_frames):
+                slot = ring.slot_of(frame0 + j, self.S, self.W)
+                codes[:, slot] = packed[j].transpose(1, 0, 2)
+                scales[:, slot] = s8[j].transpose(1, 0, 2)
+                tsc[slot] = g
+            gs.append(g)
+        for j in range(n_frames):
+            slot = ring.slot_of(frame0 + j, self.S, self.W)
+            self.slot_frame[slot] = frame0 + j
+            self.slot_shot[slot] = shots[j]
+        return tuple(gs)
+
+    def decode_slot(self, slot):
+        """(k_hat, v_hat) float32 [H][Tc][D] of one slot."""
+        out = []
+        for codes, scales, tsc in ((self.k_codes, self.k_scales, self.k_tscale),
+                                   (self.v_codes, self.v_scales, self.v_tscale)):
+            c = nvfp4.unpack_nibbles(codes[:, slot])
+            out.append(nvfp4.decode_blocks(c, scales[:, slot], tsc[slot]))
+        return tuple(out)
+
+    # ------------------------------------------------------------ positions
+    def positions(self, frames, f1):
+        return np.array([ring.rel_pos(f, f1, self.S, self.W) for f in frames])
+
+    def rope_queries(self, q, q_frame0, n_q_frames):
+        """Rotate q[n_q_frames*T][H][D] by the cache-relative positions of its
+        frames; float64 result."""
+        f1 = q_frame0 + n_q_frames
+        pos = self.positions(range(q_frame0, f1), f1)
+        pos_tok = np.repeat(pos, self.T)[:, None]           # [Nq, 1] over heads
+        return rope.rotate(q, pos_tok, self.rot_dim, self.base)
+
+    # ------------------------------------------------------------ attention
+    def visible_slots(self, f1):
+        ws = ring.window_start(f1, self.S, self.W)
+        out = []
+        for slot in range(self.S + self.W):
+            kf = int(self.slot_frame[slot])
+            if 0 <= kf < f1 and (kf < self.S or kf >= ws):
+                out.append((slot, kf))
+        return out
+
+    def attention(self, q, q_frame0, n_q_frames, q_shots, scale=None,
+                  return_probs=False, rows=None, heads=None):
+        """Chunk attention for query frames q_frame0 .. +n_q_frames-1.
+
+        q: float32 values [n_q_frames*T][H][D] before rotation.
+        rows / heads: optional subsets of query tokens / heads to compute
+        (each output element depends only on its own query row and head).
+        Returns float64 o[len(rows)][len(heads)][D] (all rows and heads by
+        default)."""
+        H, D, T, S, W, C = self.H, self.D, self.T, self.S, self.W, self.C
+        f1 = q_frame0 + n_q_frames
+        rows = np.arange(n_q_frames * T) if rows is None else np.asarray(rows)
+        heads = list(range(H)) if heads is None else list(heads)
+        qr = self.rope_queries(q, q_frame0, n_q_frames)[rows]  # [Nr][H][D]
+        slots = self.visible_slots(f1)
+        keys, vals, kpos = [], [], []
+        for slot, kf in slots:
+            kh, vh = self.decode_slot(slot)                    # [H][Tc][D]
+            keys.append(kh)
+            vals.append(vh)
+            kpos.append(np.full(self.Tc, ring.rel_pos(kf, f1, S, W)))
+        K = np.concatenate(keys, axis=1)                       # [H][Nk][D]
+        V = np.concatenate(vals, axis=1)
+        kpos = np.concatenate(kpos)
+        frame_rows = {}
+        for a, qf in enumerate(range(q_frame0, f1)):
+            per_slot = [ring.key_visible(kf, qf, f1, S, W, C,
+                                         int(self.slot_shot[slot]), int(q_shots[a]))
+                        for slot, kf in slots]
+            frame_rows[a] = np.repeat(np.array(per_slot, dtype=bool), self.Tc)
+        mask = np.stack([frame_rows[int(r) // T] for r in rows])
+        out = np.empty((len(rows), len(heads), D), np.float64)
+        probs = []
+        for hi, h in enumerate(heads):
+            kr = rope.rotate(K[h], kpos, self.rot_dim, self.base)
+            if return_probs:
+                s = (qr[:, h] @ kr.T) * (1.0 / np.sqrt(D) if scale is None else scale)
+                probs.append(att.softmax_rows(s, mask))
+            out[:, hi] = att.attend(qr[:, h], kr, V[h], mask, scale)
+        if return_probs:
+            return out, probs
+        return out
