@@ -12,12 +12,19 @@ Chains the oracle's parts into the three operations of the path:
   * attention: decode the cache and attend with block-causal, window and
     shot masks (evermx.com, "Multi-Shot Generation").
 
-Cache layout (the byte layout the GPU library must reproduce bit for bit):
-  k_codes, v_codes   uint8 [H][S+W][Tc][D/2]   two E2M1 codes per byte
-  k_scales, v_scales uint8 [H][S+W][Tc][D/16]  E4M3 block-scale codes
-  k_tscale, v_tscale float32 [S+W]             tensor scale g of the frame
-  slot_frame         int32 [S+W]               frame held, -1 when empty
-  slot_shot          int32 [S+W]               shot id of that frame
+Cache layout (the byte layout the GPU library must reproduce bit for bit).
+Keys are stored token-major, values dimension-major; both keep NVFP4 blocks
+of 16 consecutive elements along D.  Tv = Tc rounded up to a multiple of 32;
+value entries of the padding tokens Tc..Tv-1 are zero.
+  k_codes   uint8 [H][S+W][Tc][D/2]   key codes; element 2j of a row in the
+                                      low nibble, 2j+1 in the high nibble
+  k_scales  uint8 [H][S+W][Tc][D/16]  E4M3 scale of each key block
+  v_codes   uint8 [H][S+W][D][Tv/2]   value codes of one dimension d across
+                                      tokens; token 2j low nibble, 2j+1 high
+  v_scales  uint8 [H][S+W][D/16][Tv]  E4M3 scale of value block b of each token
+  k_tscale, v_tscale float32 [S+W]    tensor scale g of the frame
+  slot_frame         int32 [S+W]      frame held, -1 when empty
+  slot_shot          int32 [S+W]      shot id of that frame
 The cache holds keys before rotation; keys are rotated after decoding with
 the positions of the current step, so codes are written once and never
 re-quantized when the window slides (reading of "KV-cache relative RoPE").
@@ -49,10 +56,11 @@ class OracleCache:
         self.rot_dim = D if rot_dim is None else rot_dim
         self.base = base
         n = S + W
+        self.Tv = -(-self.Tc // 32) * 32
         self.k_codes = np.zeros((H, n, self.Tc, D // 2), np.uint8)
-        self.v_codes = np.zeros((H, n, self.Tc, D // 2), np.uint8)
+        self.v_codes = np.zeros((H, n, D, self.Tv // 2), np.uint8)
         self.k_scales = np.zeros((H, n, self.Tc, D // 16), np.uint8)
-        self.v_scales = np.zeros((H, n, self.Tc, D // 16), np.uint8)
+        self.v_scales = np.zeros((H, n, D // 16, self.Tv), np.uint8)
         self.k_tscale = np.ones(n, np.float32)
         self.v_tscale = np.ones(n, np.float32)
         self.slot_frame = np.full(n, -1, np.int32)
@@ -75,17 +83,23 @@ class OracleCache:
         """Quantize K, V ([n_frames*T][H][D], float32 values) into the slots of
         frames frame0 .. frame0+n_frames-1.  Returns (g_k, g_v)."""
         gs = []
-        for idx, (x, codes, scales, tsc) in enumerate((
-                (k, self.k_codes, self.k_scales, self.k_tscale),
-                (v, self.v_codes, self.v_scales, self.v_tscale))):
-            xk = self.kept(x, n_frames)
+        for idx, (x, tsc) in enumerate(((k, self.k_tscale), (v, self.v_tscale))):
+            xk = self.kept(x, n_frames)                        # [n][Tc][H][D]
             g = nvfp4.tensor_scale(xk) if tscale is None else np.float32(tscale[idx])
-            c, s8 = nvfp4.encode_blocks(xk, g)
-            packed = nvfp4.pack_nibbles(c)
+            c, s8 = nvfp4.encode_blocks(xk, g)                 # codes per element
             for j in range(n_frames):
                 slot = ring.slot_of(frame0 + j, self.S, self.W)
-                codes[:, slot] = packed[j].transpose(1, 0, 2)
-                scales[:, slot] = s8[j].transpose(1, 0, 2)
+                cj = c[j].transpose(1, 0, 2)                   # [H][Tc][D]
+                sj = s8[j].transpose(1, 0, 2)                  # [H][Tc][D/16]
+                if idx == 0:
+                    self.k_codes[:, slot] = nvfp4.pack_nibbles(cj)
+                    self.k_scales[:, slot] = sj
+                else:
+                    pad = self.Tv - self.Tc
+                    ct = np.pad(cj.transpose(0, 2, 1), ((0, 0), (0, 0), (0, pad)))
+                    self.v_codes[:, slot] = nvfp4.pack_nibbles(ct)      # [H][D][Tv/2]
+                    self.v_scales[:, slot] = np.pad(sj.transpose(0, 2, 1),
+                                                    ((0, 0), (0, 0), (0, pad)))
                 tsc[slot] = g
             gs.append(g)
         for j in range(n_frames):
@@ -96,12 +110,13 @@ class OracleCache:
 
     def decode_slot(self, slot):
         """(k_hat, v_hat) float32 [H][Tc][D] of one slot."""
-        out = []
-        for codes, scales, tsc in ((self.k_codes, self.k_scales, self.k_tscale),
-                                   (self.v_codes, self.v_scales, self.v_tscale)):
-            c = nvfp4.unpack_nibbles(codes[:, slot])
-            out.append(nvfp4.decode_blocks(c, scales[:, slot], tsc[slot]))
-        return tuple(out)
+        kh = nvfp4.decode_blocks(nvfp4.unpack_nibbles(self.k_codes[:, slot]),
+                                 self.k_scales[:, slot], self.k_tscale[slot])
+        cv = nvfp4.unpack_nibbles(self.v_codes[:, slot])[:, :, :self.Tc]   # [H][D][Tc]
+        sv = self.v_scales[:, slot][:, :, :self.Tc]                        # [H][D/16][Tc]
+        vh = nvfp4.decode_blocks(cv.transpose(0, 2, 1), sv.transpose(0, 2, 1),
+                                 self.v_tscale[slot])
+        return kh, vh
 
     # ------------------------------------------------------------ positions
     def positions(self, frames, f1):
