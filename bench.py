@@ -1,0 +1,213 @@
+"""Benchmark: FP4-KV chunk attention, latent frames/s per layer, on one GPU.
+
+One step = the whole hot path for one chunk of one attention layer, in
+steady state (sink + full window):
+    fp4kv_rope_rel(Q) -> fp4kv_quantize_append(K, V) -> fp4kv_attention_chunk
+on seeded synthetic inputs already resident in device memory.  The stream
+keeps going (the ring wraps); inputs rotate over 8 pre-drawn chunks.
+
+Workload (default): one layer shaped like the 1.3B generator: 12 heads,
+head_dim 128, 1560 tokens/frame, chunk 3 frames, sink 3 + window 12 frames,
+bf16 inputs ~N(0,1) with 1% outliers x20.  --workload picks another.
+
+Printed: one JSON line.  value = frames/s of one layer = C * K / time of K
+steps.  roofline = the attention kernel (the dominant one): algorithmic
+FLOP per launch 4*H*Nq*Nk*D / its mean duration from HIP events on the
+launch stream, against the 2.5 PFLOP/s dense f16/bf16 MFMA peak.
+roofline_codec = the two append kernels: algorithmic bytes (kept K and V
+read once, codes and scales written once) / their mean duration, against
+8 TB/s.  cpu_baseline = the CPU oracle on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "FP4-KV chunk attention latent frames/s per layer; HBM GB/s & MFMA % of peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="l13b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="per-launch HBM bytes measured with rocprofv3 counters")
+    return ap.parse_args()
+
+
+def workload_desc(w):
+    out = (f"{w.name}: H{w.H} D{w.D} T{w.T} C{w.C} S{w.S} W{w.W}"
+           + (f" token_stride {w.token_stride}" if w.token_stride > 1 else "")
+           + (f" shots of {w.shot_len} frames" if w.shot_len else "")
+           + (f", {w.outlier_p:.0%} outliers x{w.outlier_scale:g}" if w.outlier_p else ""))
+    return out
+
+
+def cpu_baseline(w):
+    """The oracle as it stands on a few heads of one steady-state step (append
+    of those heads' K/V chunk plus attention of all their query rows), scaled
+    to all heads."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from fp4_kv_cache_fp4kv_amd import workloads as wl
+    from oracle.stream import OracleCache
+
+    hs = min(w.H, 4)
+    one = wl.Workload(w.name + "_sample", H=hs, D=w.D, T=w.T, C=w.C, S=w.S, W=w.W,
+                      n_frames=w.S + w.W + w.C, seed=w.seed, dtype=w.dtype,
+                      outlier_p=w.outlier_p, outlier_scale=w.outlier_scale,
+                      shot_len=w.shot_len, token_stride=w.token_stride)
+    oc = OracleCache.for_workload(one)
+    steps = one.n_chunks
+    inputs = [wl.draw_qkv(one, c) for c in range(steps)]
+    for c in range(steps - 1):
+        f0, n = one.chunk_frames(c)
+        (_, _), (k, _), (v, _) = inputs[c]
+        oc.append(k, v, f0, n, [one.shot_of(f) for f in range(f0, f0 + n)])
+    c = steps - 1
+    f0, n = one.chunk_frames(c)
+    (q, _), (k, _), (v, _) = inputs[c]
+    shots = [one.shot_of(f) for f in range(f0, f0 + n)]
+    t0 = time.perf_counter()
+    oc.append(k, v, f0, n, shots)
+    oc.attention(q, f0, n, shots)
+    dt = time.perf_counter() - t0
+    step_s = dt * w.H / hs
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(w.C / step_s, 4), "unit": "latent frames/s per layer",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{hs} of {w.H} heads of one steady-state step (append + attention of "
+                      f"{n * w.T} query rows over {(w.S + w.W) * w.Tc} keys per head), "
+                      f"{dt:.1f} s, scaled to all heads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by head or by time, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from fp4_kv_cache_fp4kv_amd import api
+    from fp4_kv_cache_fp4kv_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    gc = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride, device="cuda:0")
+
+    def dev_t(vals, bits):
+        if bits is not None:
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(vals).to(dev)
+
+    n_sets = 8
+    sets = []
+    n_tok = w.C * w.T
+    for c in range(n_sets):
+        sets.append(tuple(dev_t(*wl.draw(w, c, tid, n_tokens=n_tok))
+                          for tid in (wl.Q_ID, wl.K_ID, wl.V_ID)))
+    qrot = torch.empty((w.C * w.T, w.H, w.D), dtype=torch.float32, device=dev)
+    out = torch.empty((w.C * w.T, w.H, w.D), dtype=torch.bfloat16, device=dev)
+    first = -(-(w.S + w.W) // w.C)       # first chunk step with a full window
+
+    ev = {k: [] for k in ("a0", "a1", "c0", "c1")}
+
+    def step(c, record):
+        q, k, v = sets[c % n_sets]
+        f0 = c * w.C
+        shots = [w.shot_of(f) for f in range(f0, f0 + w.C)]
+        if record:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record()
+        api.quantize_append(gc, k, v, f0, w.C, shots)
+        if record:
+            e[1].record()
+        api.rope_rel(q, api.cache_positions(w.S, w.W, f0, w.C), w.T, gc.cos_sin, out=qrot)
+        if record:
+            e[2].record()
+        api.attention_chunk(gc, qrot, f0, w.C, shots, out=out)
+        if record:
+            e[3].record()
+            ev["c0"].append(e[0]); ev["c1"].append(e[1])
+            ev["a0"].append(e[2]); ev["a1"].append(e[3])
+
+    for c in range(first):                # fill the sink and window
+        step(c, False)
+    c = first
+    for _ in range(args.warmup):
+        step(c, False)
+        c += 1
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step(c, True)
+        c += 1
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    attn_ms = sum(a.elapsed_time(b) for a, b in zip(ev["a0"], ev["a1"])) / args.steps
+    codec_ms = sum(a.elapsed_time(b) for a, b in zip(ev["c0"], ev["c1"])) / args.steps
+
+    Nq, Nk = w.C * w.T, (w.S + w.W) * w.Tc
+    flops = 4.0 * w.H * Nq * Nk * w.D
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    es = 2 if w.dtype == "bf16" else 4
+    kept = 2 * w.C * w.Tc * w.H * w.D
+    codec_bytes = kept * es + kept * (0.5 + 1.0 / 16.0)
+    codec_gbs = codec_bytes / (codec_ms * 1e-3) / 1e9
+
+    traffic = None
+    try:
+        tj = json.load(open(args.traffic_json))
+        if tj.get("workload") == w.name:
+            traffic = tj.get("attention_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+
+    res = {
+        "metric": METRIC,
+        "value": round(w.C / (ms_step * 1e-3), 3),
+        "unit": "latent frames/s per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": workload_desc(w), "query_rows": Nq, "keys": Nk,
+                   "frames_per_step": w.C, "attention_ms": round(attn_ms, 4),
+                   "append_ms": round(codec_ms, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": traffic},
+        "roofline_codec": {"bound": "hbm", "achieved": round(codec_gbs, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(codec_gbs / HBM_PEAK_GBS, 4),
+                           "bytes": int(codec_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,240 @@
+// C ABI: host-side validation, then launches on the caller's stream.
+// Every check runs before anything is enqueued; see include/fp4kv.h.
+#include <math.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "fp4kv.h"
+#include "internal.hpp"
+
+using namespace fp4kv;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Value rows hold Tc tokens padded to a multiple of 32.
+int padded_tokens(const fp4kv_cache *c) {
+  const int tc = c->tokens_per_frame / c->token_stride;
+  return (tc + 31) / 32 * 32;
+}
+
+// Shape checks of a cache descriptor (no pointer reads).
+int check_shape(const fp4kv_cache *c) {
+  if (!c) return FP4KV_EINVAL;
+  if (c->format_tag != FP4KV_FORMAT_NVFP4_V1) return FP4KV_EFORMAT;
+  if (c->n_heads < 1 || c->tokens_per_frame < 1 || c->chunk_frames < 1 || c->sink_frames < 0)
+    return FP4KV_EINVAL;
+  if (c->head_dim != 64 && c->head_dim != 128) return FP4KV_ESHAPE;
+  if (c->token_stride != 1 && c->token_stride != 2) return FP4KV_EINVAL;
+  if (c->tokens_per_frame % c->token_stride != 0) return FP4KV_ESHAPE;
+  if (c->window_frames < c->chunk_frames) return FP4KV_ESHAPE;
+  if (c->sink_frames + c->window_frames > FP4KV_MAX_SLOTS) return FP4KV_ESHAPE;
+  if (c->rot_dim < 0 || c->rot_dim > c->head_dim || (c->rot_dim & 1)) return FP4KV_EINVAL;
+  const long long rows = (long long)c->n_heads * (c->sink_frames + c->window_frames) *
+                         (c->tokens_per_frame / c->token_stride);
+  if (rows * c->head_dim > (1ll << 40)) return FP4KV_ESHAPE;
+  return FP4KV_OK;
+}
+
+int check_buffers(const fp4kv_cache *c) {
+  const void *ptrs[] = {c->k_codes, c->v_codes, c->k_scales, c->v_scales,
+                        c->k_tscale, c->v_tscale, c->slot_frame, c->slot_shot};
+  for (const void *p : ptrs) {
+    if (!p) return FP4KV_EINVAL;
+    if (!aligned16(p)) return FP4KV_EALIGN;
+  }
+  return FP4KV_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? FP4KV_OK : FP4KV_EDEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+const char *fp4kv_strerror(int status) {
+  switch (status) {
+    case FP4KV_OK: return "ok";
+    case FP4KV_EINVAL: return "invalid argument (null pointer or value out of range)";
+    case FP4KV_ESHAPE: return "inconsistent shapes";
+    case FP4KV_EALIGN: return "pointer not 16-byte aligned";
+    case FP4KV_EFORMAT: return "cache descriptor has an unknown format tag";
+    case FP4KV_EDEVICE: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int fp4kv_abi_version(void) { return kAbiVersion; }
+
+int fp4kv_cache_nbytes(const fp4kv_cache *c, size_t out[6]) {
+  int st = check_shape(c);
+  if (st) return st;
+  if (!out) return FP4KV_EINVAL;
+  const size_t slots = (size_t)(c->sink_frames + c->window_frames);
+  const size_t tc = (size_t)(c->tokens_per_frame / c->token_stride);
+  const size_t tv = (size_t)padded_tokens(c);
+  const size_t hs = (size_t)c->n_heads * slots, d = (size_t)c->head_dim;
+  out[0] = hs * tc * (d / 2);
+  out[1] = hs * d * (tv / 2);
+  out[2] = hs * tc * (d / 16);
+  out[3] = hs * (d / 16) * tv;
+  out[4] = slots * sizeof(float);
+  out[5] = slots * sizeof(int32_t);
+  return FP4KV_OK;
+}
+
+int fp4kv_cache_reset(const fp4kv_cache *c, void *stream) {
+  int st = check_shape(c);
+  if (st) return st;
+  if ((st = check_buffers(c))) return st;
+  return from_hip(launch_cache_reset(*c, (hipStream_t)stream));
+}
+
+size_t fp4kv_append_workspace_bytes(void) { return kWsBytes; }
+
+int fp4kv_quantize_append(const fp4kv_cache *c, const void *k, const void *v, int in_dtype,
+                          int32_t frame0, int32_t n_frames, const int32_t *frame_shot,
+                          const float *tscale_in, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  int st = check_shape(c);
+  if (st) return st;
+  if ((st = check_buffers(c))) return st;
+  if (!k || !v || !frame_shot || !workspace) return FP4KV_EINVAL;
+  if (in_dtype != FP4KV_F32 && in_dtype != FP4KV_BF16) return FP4KV_EINVAL;
+  if (frame0 < 0 || n_frames < 1 || n_frames > c->chunk_frames || n_frames > FP4KV_MAX_FRAMES)
+    return FP4KV_EINVAL;
+  if ((long long)frame0 + n_frames > (1ll << 30)) return FP4KV_EINVAL;
+  if (workspace_bytes < kWsBytes) return FP4KV_ESHAPE;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(workspace)) return FP4KV_EALIGN;
+  if (tscale_in && ((uintptr_t)tscale_in & 3u)) return FP4KV_EALIGN;
+
+  AppendParams p;
+  memset(&p, 0, sizeof(p));
+  p.x[0] = k;
+  p.x[1] = v;
+  p.codes[0] = c->k_codes;
+  p.codes[1] = c->v_codes;
+  p.scales[0] = c->k_scales;
+  p.scales[1] = c->v_scales;
+  p.tscale[0] = c->k_tscale;
+  p.tscale[1] = c->v_tscale;
+  p.slot_frame = c->slot_frame;
+  p.slot_shot = c->slot_shot;
+  p.tscale_in = tscale_in;
+  p.ws_counter = (uint32_t *)((uint8_t *)workspace + kWsCounterOff);
+  p.ws_scale = (float *)((uint8_t *)workspace + kWsScaleOff);
+  p.ws_partial = (uint32_t *)((uint8_t *)workspace + kWsPartialOff);
+  p.H = c->n_heads;
+  p.D = c->head_dim;
+  p.T = c->tokens_per_frame;
+  p.stride = c->token_stride;
+  p.Tc = c->tokens_per_frame / c->token_stride;
+  p.Tv = padded_tokens(c);
+  p.S = c->sink_frames;
+  p.W = c->window_frames;
+  p.n_slots = c->sink_frames + c->window_frames;
+  p.frame0 = frame0;
+  p.n_frames = n_frames;
+  p.in_bf16 = in_dtype == FP4KV_BF16;
+  for (int j = 0; j < n_frames; ++j) p.shot[j] = frame_shot[j];
+  return from_hip(launch_append(p, (hipStream_t)stream));
+}
+
+int fp4kv_rope_table(float *cos_sin, int32_t n_pos, int32_t rot_dim, double base) {
+  if (!cos_sin || n_pos < 1 || rot_dim < 2 || (rot_dim & 1) || !(base > 1.0)) return FP4KV_EINVAL;
+  const int half = rot_dim / 2;
+  for (int p = 0; p < n_pos; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double theta = pow(base, -2.0 * i / (double)rot_dim);
+      const double phi = (double)p * theta;
+      cos_sin[((size_t)p * half + i) * 2 + 0] = (float)cos(phi);
+      cos_sin[((size_t)p * half + i) * 2 + 1] = (float)sin(phi);
+    }
+  return FP4KV_OK;
+}
+
+int fp4kv_rope_rel(const void *x, int in_dtype, void *y, int out_dtype, int64_t n_tokens,
+                   int32_t n_heads, int32_t head_dim, int32_t tokens_per_frame, int32_t pos0,
+                   int32_t rot_dim, const float *cos_sin, int32_t n_pos, void *stream) {
+  if (!x || !y || !cos_sin) return FP4KV_EINVAL;
+  if (in_dtype != FP4KV_F32 && in_dtype != FP4KV_BF16) return FP4KV_EINVAL;
+  if (out_dtype != FP4KV_F32 && out_dtype != FP4KV_BF16) return FP4KV_EINVAL;
+  if (n_tokens < 0 || n_heads < 1 || tokens_per_frame < 1 || pos0 < 0 || n_pos < 1)
+    return FP4KV_EINVAL;
+  if (head_dim < 8 || head_dim % 8) return FP4KV_ESHAPE;
+  if (rot_dim < 0 || rot_dim > head_dim || (rot_dim & 1)) return FP4KV_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)cos_sin & 7u)) return FP4KV_EALIGN;
+  if (x == y && in_dtype != out_dtype) return FP4KV_EINVAL;
+  if (n_tokens == 0) return FP4KV_OK;
+  if ((long long)pos0 + (n_tokens - 1) / tokens_per_frame >= n_pos) return FP4KV_ESHAPE;
+  if (n_tokens * n_heads * (long long)head_dim > (1ll << 40)) return FP4KV_ESHAPE;
+  RopeParams p;
+  p.x = x;
+  p.y = y;
+  p.out_f32 = out_dtype == FP4KV_F32;
+  p.cos_sin = cos_sin;
+  p.n_tokens = n_tokens;
+  p.H = n_heads;
+  p.D = head_dim;
+  p.T = tokens_per_frame;
+  p.pos0 = pos0;
+  p.rot_dim = rot_dim;
+  p.in_bf16 = in_dtype == FP4KV_BF16;
+  return from_hip(launch_rope(p, (hipStream_t)stream));
+}
+
+int fp4kv_attention_chunk(const fp4kv_cache *c, const void *q_rot, int q_dtype, void *o,
+                          int out_dtype, int32_t q_frame0, int32_t n_q_frames,
+                          const int32_t *q_shot, const float *cos_sin, int32_t n_pos,
+                          float softmax_scale, void *stream) {
+  int st = check_shape(c);
+  if (st) return st;
+  if ((st = check_buffers(c))) return st;
+  if (!q_rot || !o || !q_shot || !cos_sin) return FP4KV_EINVAL;
+  if (out_dtype != FP4KV_F32 && out_dtype != FP4KV_BF16) return FP4KV_EINVAL;
+  if (q_dtype != FP4KV_F32 && q_dtype != FP4KV_BF16) return FP4KV_EINVAL;
+  if (q_frame0 < 0 || n_q_frames < 1 || n_q_frames > FP4KV_MAX_FRAMES) return FP4KV_EINVAL;
+  if ((long long)q_frame0 + n_q_frames > (1ll << 30)) return FP4KV_EINVAL;
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return FP4KV_EINVAL;
+  if (n_pos < c->sink_frames + c->window_frames) return FP4KV_ESHAPE;
+  if (!aligned16(q_rot) || !aligned16(o) || ((uintptr_t)cos_sin & 7u)) return FP4KV_EALIGN;
+  if (q_rot == o) return FP4KV_EINVAL;
+  const long long nq = (long long)n_q_frames * c->tokens_per_frame;
+  if (nq > (1ll << 30) || nq * c->n_heads > (1ll << 31)) return FP4KV_ESHAPE;
+
+  AttnParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q_rot;
+  p.q_f32 = q_dtype == FP4KV_F32;
+  p.o = o;
+  p.k_codes = c->k_codes;
+  p.v_codes = c->v_codes;
+  p.k_scales = c->k_scales;
+  p.v_scales = c->v_scales;
+  p.k_tscale = c->k_tscale;
+  p.v_tscale = c->v_tscale;
+  p.slot_frame = c->slot_frame;
+  p.slot_shot = c->slot_shot;
+  p.cos_sin = cos_sin;
+  p.H = c->n_heads;
+  p.T = c->tokens_per_frame;
+  p.Tc = c->tokens_per_frame / c->token_stride;
+  p.Tv = padded_tokens(c);
+  p.C = c->chunk_frames;
+  p.S = c->sink_frames;
+  p.W = c->window_frames;
+  p.n_slots = c->sink_frames + c->window_frames;
+  p.rot_dim = c->rot_dim;
+  p.q_frame0 = q_frame0;
+  p.n_q_frames = n_q_frames;
+  p.Nq = (int)nq;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  for (int j = 0; j < n_q_frames; ++j) p.q_shot[j] = q_shot[j];
+  return from_hip(launch_attention(p, c->head_dim, out_dtype == FP4KV_F32, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Internal launch interfaces between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4kv.h"
+
+namespace fp4kv {
+
+// Number of partial maxima per tensor in the append workspace.
+constexpr int kAmaxBlocks = 512;
+
+// Workspace layout of fp4kv_quantize_append (bytes from the base):
+//   [0, 8)      uint32 arrival counters for K and V (zero between calls)
+//   [16, 24)    float tensor scales g_k, g_v computed by the amax pass
+//   [64, ...)   uint32 partial maxima [2][kAmaxBlocks]
+constexpr size_t kWsCounterOff = 0;
+constexpr size_t kWsScaleOff = 16;
+constexpr size_t kWsPartialOff = 64;
+constexpr size_t kWsBytes = kWsPartialOff + 2 * kAmaxBlocks * sizeof(uint32_t);
+
+struct AppendParams {
+  const void *x[2];        // K, V inputs [n_frames*T][H][D]
+  uint8_t *codes[2];
+  uint8_t *scales[2];
+  float *tscale[2];
+  int32_t *slot_frame, *slot_shot;
+  const float *tscale_in;  // device [2] or null
+  uint32_t *ws_counter;    // [2]
+  float *ws_scale;         // [2]
+  uint32_t *ws_partial;    // [2][kAmaxBlocks]
+  int H, D, T, stride, Tc, Tv, S, W, n_slots, frame0, n_frames;
+  int in_bf16;
+  int32_t shot[FP4KV_MAX_FRAMES];
+};
+
+struct RopeParams {
+  const void *x;
+  void *y;
+  const float *cos_sin;
+  long long n_tokens;
+  int H, D, T, pos0, rot_dim, in_bf16, out_f32;
+};
+
+struct AttnParams {
+  const void *q;           // rotated queries [Nq][H][D], float32 or bf16
+  void *o;                 // [Nq][H][D]
+  const uint8_t *k_codes, *v_codes, *k_scales, *v_scales;
+  const float *k_tscale, *v_tscale;
+  const int32_t *slot_frame, *slot_shot;
+  const float *cos_sin;
+  int H, T, Tc, Tv, C, S, W, n_slots, rot_dim;
+  int q_frame0, n_q_frames, Nq, q_f32;
+  float scale_log2;        // softmax_scale * log2(e)
+  int32_t q_shot[FP4KV_MAX_FRAMES];
+};
+
+hipError_t launch_cache_reset(const fp4kv_cache &c, hipStream_t s);
+hipError_t launch_append(const AppendParams &p, hipStream_t s);
+hipError_t launch_rope(const RopeParams &p, hipStream_t s);
+hipError_t launch_attention(const AttnParams &p, int head_dim, int out_f32, hipStream_t s);
+
+}  // namespace fp4kv

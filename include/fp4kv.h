@@ -1,0 +1,250 @@
+/*
+ * fp4kv.h - C ABI of the MI355X (gfx950) FP4 KV-cache chunk-attention library.
+ *
+ * The library implements the per-step hot path of chunk-wise causal attention
+ * for autoregressive long-video diffusion over a 4-bit NVFP4 KV cache, the
+ * mechanisms the LongLive 2.0 pages name:
+ *   - an NVFP4 KV cache written in place ("in-place quantized KV-cache
+ *     updates"; hysenlabs.com, section "NVFP4, sequence parallel and the async
+ *     decode path"; evermx.com, section "NVFP4 Quantization End-to-End");
+ *   - KV-cache relative RoPE (aiany.app, section "What Sets It Apart";
+ *     refft.com, question "How do KV-cache relative RoPE and TriAttention work
+ *     together ...");
+ *   - attention sinks plus a bounded window (heatdrop.ai, section "What it
+ *     does") with multi-shot masking (evermx.com, section "Multi-Shot
+ *     Generation");
+ *   - FP4 KV dequantization fused into attention ("faster FP4 KV
+ *     dequantization", hysenlabs.com, same section as above).
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are HIP device pointers owned by the caller;
+ *     the library never allocates, frees or keeps them.  Pointers marked
+ *     "host" are read during the call only.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; no call synchronizes the device.
+ *   - Every call validates its arguments on the host before enqueuing
+ *     anything.  On a negative status nothing was enqueued, except
+ *     FP4KV_EDEVICE, which reports a launch error returned by HIP.
+ *   - Faults inside kernels (e.g. device pointers that are too small) are not
+ *     detected by the library and surface at the caller's next
+ *     synchronization.
+ *   - Tensors are dense, row-major, with the innermost dimension last.
+ *   - Inputs must be finite; NaN and Inf inputs give unspecified codes.
+ *   - The library keeps no mutable global state, so calls on different
+ *     streams and caches may run concurrently.  Calls that touch the same
+ *     cache buffers must be ordered by the caller (same stream or events).
+ */
+#ifndef FP4KV_H
+#define FP4KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+#define FP4KV_OK        0
+#define FP4KV_EINVAL  (-1)  /* null pointer, or a value out of its range      */
+#define FP4KV_ESHAPE  (-2)  /* sizes inconsistent with each other             */
+#define FP4KV_EALIGN  (-3)  /* pointer not aligned as documented              */
+#define FP4KV_EFORMAT (-4)  /* cache descriptor carries an unknown format tag */
+#define FP4KV_EDEVICE (-5)  /* HIP reported an error when launching           */
+
+/* ---------------------------------------------------------------- dtypes */
+#define FP4KV_F32  0
+#define FP4KV_BF16 1
+
+/* Format tag of the NVFP4 cache layout described below. */
+#define FP4KV_FORMAT_NVFP4_V1 0x3146564Eu
+
+/* Limits.  Frames per call and cache slots are passed to kernels by value. */
+#define FP4KV_MAX_FRAMES 64   /* frames per append or attention call      */
+#define FP4KV_MAX_SLOTS  64   /* sink + window frames (S + W)             */
+
+/*
+ * fp4kv_cache - descriptor of one layer's NVFP4 KV cache.
+ *
+ * The cache holds S sink frames (the first S frames of the stream, never
+ * evicted) and a ring of W window frames that includes the current chunk:
+ * frame f lives in slot f if f < S, else in slot S + ((f - S) mod W).
+ * Each cached frame keeps Tc = tokens_per_frame / token_stride tokens
+ * (in-frame token t is kept iff t mod token_stride == 0).
+ *
+ * Keys are stored BEFORE rotary rotation; attention rotates them by their
+ * cache-relative position at every step, so stored codes never change when
+ * the window slides.
+ *
+ * NVFP4 blocks are 16 consecutive elements along D for keys and values.
+ * Keys are stored token-major; values are stored dimension-major so that the
+ * attention kernel reads, for one dimension, consecutive tokens (the
+ * reduction axis of P.V).  Tv = Tc rounded up to a multiple of 32; value
+ * entries of padding tokens Tc..Tv-1 are written as zeros and never read
+ * unmasked.
+ *
+ * Buffers (device, caller-owned, 16-byte aligned, contiguous):
+ *   k_codes   uint8 [H][S+W][Tc][D/2]   E2M1 codes of a key row, two per byte:
+ *                                       element 2j in the low nibble, sign in
+ *                                       bit 3 of each nibble
+ *   k_scales  uint8 [H][S+W][Tc][D/16]  E4M3 (OCP E4M3FN) scale per key block
+ *   v_codes   uint8 [H][S+W][D][Tv/2]   E2M1 codes of one value dimension
+ *                                       across tokens: token 2j low nibble,
+ *                                       token 2j+1 high nibble
+ *   v_scales  uint8 [H][S+W][D/16][Tv]  E4M3 scale of value block b of a token
+ *   k_tscale, v_tscale  float [S+W]     FP32 tensor scale of the append that
+ *                                       wrote the slot
+ *   slot_frame          int32 [S+W]     frame in the slot, -1 when empty
+ *   slot_shot           int32 [S+W]     shot id of that frame
+ * A decoded element is sign * E2M1(code) * E4M3(scale) * tensor_scale.
+ * These buffers are opaque bytes: never cast or convert them.
+ */
+typedef struct fp4kv_cache {
+  uint32_t format_tag;        /* FP4KV_FORMAT_NVFP4_V1                        */
+  int32_t  n_heads;           /* H >= 1                                      */
+  int32_t  head_dim;          /* D: 64 or 128                                */
+  int32_t  tokens_per_frame;  /* T >= 1                                      */
+  int32_t  token_stride;      /* 1 or 2; T % token_stride == 0               */
+  int32_t  chunk_frames;      /* C >= 1: frames per chunk (block-causal unit) */
+  int32_t  sink_frames;       /* S >= 0                                      */
+  int32_t  window_frames;     /* W >= C; S + W <= FP4KV_MAX_SLOTS            */
+  int32_t  rot_dim;           /* even, 0 <= rot_dim <= D: rotated leading dims */
+  uint8_t *k_codes, *v_codes;
+  uint8_t *k_scales, *v_scales;
+  float   *k_tscale, *v_tscale;
+  int32_t *slot_frame, *slot_shot;
+} fp4kv_cache;
+
+/* Human-readable text for a status code (static storage). */
+const char *fp4kv_strerror(int status);
+
+/* Library ABI version (increments when any signature or layout changes). */
+int fp4kv_abi_version(void);
+
+/*
+ * fp4kv_cache_nbytes - byte sizes of the cache buffers (host only, no GPU).
+ * out[0] = k_codes, out[1] = v_codes, out[2] = k_scales, out[3] = v_scales,
+ * out[4] = each of k_tscale / v_tscale, out[5] = each of slot_frame /
+ * slot_shot.  Pointer fields of `c` are not read.
+ */
+int fp4kv_cache_nbytes(const fp4kv_cache *c, size_t out[6]);
+
+/*
+ * fp4kv_cache_reset - mark every slot empty: slot_frame := -1,
+ * slot_shot := 0, k_tscale = v_tscale := 1.  Codes and scales are left as
+ * they are (an empty slot is never read).  Uses a fill kernel, so it may be
+ * captured in a HIP graph.
+ */
+int fp4kv_cache_reset(const fp4kv_cache *c, void *stream);
+
+/* Bytes of device workspace fp4kv_quantize_append needs (constant). */
+size_t fp4kv_append_workspace_bytes(void);
+
+/*
+ * fp4kv_quantize_append - NVFP4-encode a chunk of new keys and values and
+ * write it in place into the cache slots of frames frame0 .. frame0+n-1
+ * ("in-place quantized KV-cache updates"; hysenlabs.com, section "NVFP4,
+ * sequence parallel and the async decode path").
+ *
+ *   k, v        device, [n_frames * T][H][D] of in_dtype (FP4KV_F32 or
+ *               FP4KV_BF16), 16-byte aligned.  Only kept tokens are read.
+ *   frame0      >= 0, first frame of the chunk.
+ *   n_frames    1 .. min(C, FP4KV_MAX_FRAMES) (a partial last chunk is allowed).
+ *   frame_shot  host [n_frames]: shot id of each frame (written to slot_shot).
+ *   tscale_in   device float[2] = {g_k, g_v} to use as tensor scales (finite,
+ *               > 0), or NULL to compute g = amax / 2688 over the kept tokens
+ *               of each of K and V (g = 1 when amax = 0).
+ *   workspace   device, fp4kv_append_workspace_bytes() bytes, 16-byte
+ *               aligned.  It must be zero-filled before its first use; every
+ *               call leaves it zero-filled again.  Calls that overlap in time
+ *               must use different workspaces.
+ *
+ * Encoding, per 16-element block b along D of one (token, head) row, all in
+ * IEEE float32 with round-to-nearest-even:
+ *   d = 6 * g;  s8 = E4M3_satfinite(a_b / d)  (a_b = max |x| of the block);
+ *   S = value(s8) * g;  r = 1 / S;  code = signbit(x) << 3 | E2M1_sat(|x| * r),
+ *   with magnitude 0 when value(s8) = 0 or x = 0.
+ * Re-appending the same frames with the same data rewrites identical bytes.
+ * Slots of other frames are untouched.
+ */
+int fp4kv_quantize_append(const fp4kv_cache *c, const void *k, const void *v,
+                          int in_dtype, int32_t frame0, int32_t n_frames,
+                          const int32_t *frame_shot, const float *tscale_in,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fp4kv_rope_table - fill a rotary table on the host (no GPU):
+ *   cos_sin[p][i][0] = cos(p * base^(-2i/rot_dim)),
+ *   cos_sin[p][i][1] = sin(p * base^(-2i/rot_dim)),
+ * for p < n_pos, i < rot_dim/2, computed in double and rounded to float.
+ * cos_sin is host memory of n_pos * rot_dim * sizeof(float) bytes; copy it
+ * to the device for the calls below.
+ */
+int fp4kv_rope_table(float *cos_sin, int32_t n_pos, int32_t rot_dim, double base);
+
+/*
+ * fp4kv_rope_rel - rotate a [n_tokens][H][D] tensor by cache-relative frame
+ * positions (relative RoPE: refft.com, question "How do KV-cache relative
+ * RoPE and TriAttention work together ..."; fused RoPE: hysenlabs.com,
+ * section "NVFP4, sequence parallel and the async decode path").
+ *
+ * Token t belongs to frame t / T and is rotated by position pos0 + t / T:
+ * each pair (2i, 2i+1), i < rot_dim/2, turns by cos_sin[pos][i], i.e.
+ * (a, b) -> (a c - b s, a s + b c).  Dimensions past rot_dim are copied.
+ * Math in float32; a bf16 output is rounded to nearest even.
+ *   x         device, in_dtype (FP4KV_F32 or FP4KV_BF16), 16-byte aligned.
+ *   y         device, out_dtype (FP4KV_F32 or FP4KV_BF16), same shape; may
+ *             alias x when in_dtype == out_dtype.
+ *   cos_sin   device table from fp4kv_rope_table with n_pos rows;
+ *             pos0 + (n_tokens - 1) / T must be < n_pos.
+ * The attention kernel takes float32 rotated queries (bf16 is accepted but
+ * rounds the queries once more).
+ */
+int fp4kv_rope_rel(const void *x, int in_dtype, void *y, int out_dtype, int64_t n_tokens,
+                   int32_t n_heads, int32_t head_dim, int32_t tokens_per_frame,
+                   int32_t pos0, int32_t rot_dim, const float *cos_sin,
+                   int32_t n_pos, void *stream);
+
+/*
+ * fp4kv_attention_chunk - attention of the query frames
+ * q_frame0 .. q_frame0+n_q_frames-1 over the NVFP4 cache, with FP4
+ * dequantization fused into the attention loop.
+ *
+ * With f1 = q_frame0 + n_q_frames and ws = max(S, f1 - W), a cached frame kf
+ * is visible to query frame qf iff
+ *     0 <= kf < f1,  (kf < S or kf >= ws)                       (sink + window)
+ *     kf / C <= qf / C                                          (block-causal)
+ *     kf < S or slot_shot(kf) == q_shot[qf - q_frame0]          (multi-shot)
+ * The multi-shot rule follows evermx.com, section "Multi-Shot Generation";
+ * the sink and window follow heatdrop.ai, section "What it does".
+ * Cache-relative position: pos(f) = f if f < S else S + (f - ws), for keys
+ * and queries alike.  Scores are softmax_scale * (R(pos(qf)) q) . (R(pos(kf)) k)
+ * with k the decoded (pre-rotation) key; the output of a query row is the
+ * softmax-weighted sum of the decoded values.
+ *
+ * Arithmetic: MFMA with f16 operands and float32 accumulation.  Decoded keys
+ * and values are exact in f16 (tensor scales are applied in float32); the
+ * queries are carried as an f16 high part plus an f16 low part; softmax
+ * weights are rounded to f16.  Queries must be below 2^15 in magnitude.
+ *
+ *   q_rot   device [n_q_frames * T][H][D] of q_dtype (FP4KV_F32 or
+ *           FP4KV_BF16): queries ALREADY rotated by their cache-relative
+ *           positions (fp4kv_rope_rel with pos0 = pos(q_frame0)),
+ *           16-byte aligned.
+ *   o       device [n_q_frames * T][H][D] of out_dtype (FP4KV_F32 or
+ *           FP4KV_BF16), 16-byte aligned, must not alias q_rot.
+ *   q_shot  host [n_q_frames]: shot id of each query frame.
+ *   cos_sin device rotary table with n_pos >= S + W rows (fp4kv_rope_table,
+ *           cache->rot_dim).
+ * Rows with no visible key are written as zeros.
+ */
+int fp4kv_attention_chunk(const fp4kv_cache *c, const void *q_rot, int q_dtype, void *o,
+                          int out_dtype, int32_t q_frame0, int32_t n_q_frames,
+                          const int32_t *q_shot, const float *cos_sin,
+                          int32_t n_pos, float softmax_scale, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4KV_H */

@@ -1,0 +1,181 @@
+"""C-ABI checks that need no GPU: the built library loads, exports every
+function include/fp4kv.h declares, and rejects bad arguments on the host
+with the documented status codes before anything is enqueued."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from fp4_kv_cache_fp4kv_amd import _lib
+from fp4_kv_cache_fp4kv_amd._lib import CacheDesc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4kv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libfp4kv.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4kv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_path_calls():
+    names = declared_functions()
+    for n in ("fp4kv_quantize_append", "fp4kv_attention_chunk", "fp4kv_rope_rel"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fp4kv_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    assert set(declared_functions()) == set(_lib.EXPORTED)
+
+
+def test_ctypes_struct_matches_c_layout():
+    # uint32 + 8 int32 = 36 bytes, pointers start at 40
+    assert CacheDesc.k_codes.offset == 40
+    assert ctypes.sizeof(CacheDesc) == 40 + 8 * 8
+
+
+def _desc(**kw):
+    d = dict(format_tag=_lib.FP4KV_FORMAT_NVFP4_V1, n_heads=2, head_dim=128, tokens_per_frame=32,
+             token_stride=1, chunk_frames=3, sink_frames=3, window_frames=12, rot_dim=128)
+    d.update(kw)
+    c = CacheDesc(**d)
+    for i, name in enumerate(("k_codes", "v_codes", "k_scales", "v_scales", "k_tscale",
+                              "v_tscale", "slot_frame", "slot_shot")):
+        setattr(c, name, 0x10000 * (i + 1))   # aligned fake addresses, never dereferenced
+    return c
+
+
+def test_strerror_and_version():
+    lib = _lib.load()
+    assert lib.fp4kv_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5):
+        assert lib.fp4kv_strerror(st)
+    assert lib.fp4kv_append_workspace_bytes() >= 64
+
+
+def test_cache_nbytes():
+    lib = _lib.load()
+    out = (ctypes.c_size_t * 6)()
+    c = _desc(token_stride=2)             # T = 32 -> Tc = 16 kept tokens, Tv = 32
+    assert lib.fp4kv_cache_nbytes(ctypes.byref(c), out) == 0
+    hs = 2 * 15
+    assert list(out) == [hs * 16 * 64, hs * 128 * 16, hs * 16 * 8, hs * 8 * 32, 15 * 4, 15 * 4]
+    c = _desc(tokens_per_frame=1560)      # Tv = 1568
+    assert lib.fp4kv_cache_nbytes(ctypes.byref(c), out) == 0
+    assert out[1] == hs * 128 * 784 and out[3] == hs * 8 * 1568
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("format_tag", 0x1234, -4),
+    ("head_dim", 96, -2),
+    ("head_dim", 256, -2),
+    ("n_heads", 0, -1),
+    ("token_stride", 3, -1),
+    ("tokens_per_frame", 33, 0),       # fine with stride 1
+    ("window_frames", 2, -2),          # W < C
+    ("sink_frames", 60, -2),           # S + W > 64
+    ("rot_dim", 129, -1),
+    ("rot_dim", 7, -1),
+    ("sink_frames", -1, -1),
+])
+def test_descriptor_validation(field, value, status):
+    lib = _lib.load()
+    out = (ctypes.c_size_t * 6)()
+    c = _desc(**{field: value})
+    assert lib.fp4kv_cache_nbytes(ctypes.byref(c), out) == status
+
+
+def test_stride_must_divide_tokens():
+    lib = _lib.load()
+    out = (ctypes.c_size_t * 6)()
+    c = _desc(token_stride=2, tokens_per_frame=33)
+    assert lib.fp4kv_cache_nbytes(ctypes.byref(c), out) == -2
+
+
+def test_append_validation_before_launch():
+    lib = _lib.load()
+    c = _desc()
+    shots = (ctypes.c_int32 * 4)(0, 0, 0, 0)
+    ws = lib.fp4kv_append_workspace_bytes()
+    A = 0x100000
+    call = lambda **kw: lib.fp4kv_quantize_append(
+        ctypes.byref(kw.get("c", c)), kw.get("k", A), kw.get("v", A), kw.get("dt", 1),
+        kw.get("f0", 0), kw.get("n", 3), kw.get("shots", shots), None, kw.get("ws", A),
+        kw.get("wsb", ws), None)
+    assert call(k=None) == -1
+    assert call(dt=7) == -1
+    assert call(n=0) == -1
+    assert call(n=4) == -1            # more than a chunk
+    assert call(f0=-1) == -1
+    assert call(wsb=ws - 1) == -2
+    assert call(k=A + 8) == -3
+    assert call(ws=A + 4) == -3
+    assert call(shots=None) == -1
+    bad = _desc()
+    bad.k_codes = 0x10008
+    assert call(c=bad) == -3
+    bad.k_codes = 0
+    assert call(c=bad) == -1
+
+
+def test_rope_validation_before_launch():
+    lib = _lib.load()
+    A = 0x100000
+    call = lambda **kw: lib.fp4kv_rope_rel(
+        kw.get("x", A), kw.get("dt", 1), kw.get("y", A), kw.get("odt", 1), kw.get("n", 64), 2,
+        kw.get("D", 128), kw.get("T", 16), kw.get("pos0", 0), kw.get("rd", 128), kw.get("cs", A),
+        kw.get("npos", 4), None)
+    assert call(x=None) == -1
+    assert call(D=100) == -2
+    assert call(rd=130) == -1
+    assert call(pos0=4) == -2          # position past the table
+    assert call(n=80) == -2            # 5 frames, 4 positions
+    assert call(y=A + 2) == -3
+    assert call(dt=0) == -1            # in place needs matching dtypes
+    assert call(odt=3) == -1
+    assert call(n=0) == 0              # nothing to do, nothing launched
+
+
+def test_attention_validation_before_launch():
+    lib = _lib.load()
+    c = _desc()
+    A, B = 0x100000, 0x200000
+    shots = (ctypes.c_int32 * 4)(0, 0, 0, 0)
+    call = lambda **kw: lib.fp4kv_attention_chunk(
+        ctypes.byref(kw.get("c", c)), kw.get("q", A), kw.get("qdt", 0), kw.get("o", B),
+        kw.get("dt", 1), kw.get("f0", 0), kw.get("n", 3), kw.get("shots", shots), kw.get("cs", A),
+        kw.get("npos", 15), kw.get("scale", 0.088), None)
+    assert call(q=None) == -1
+    assert call(o=A) == -1             # aliasing
+    assert call(n=0) == -1
+    assert call(n=65) == -1
+    assert call(npos=14) == -2
+    assert call(scale=0.0) == -1
+    assert call(scale=float("inf")) == -1
+    assert call(q=A + 4) == -3
+    assert call(dt=5) == -1
+    assert call(qdt=2) == -1
+    assert call(c=_desc(format_tag=1)) == -4
+
+
+def test_rope_table_host_values():
+    import math
+    buf = (ctypes.c_float * (6 * 8))()
+    assert _lib.load().fp4kv_rope_table(buf, 6, 8, 10000.0) == 0
+    for p in range(6):
+        for i in range(4):
+            ang = p * 10000.0 ** (-2 * i / 8)
+            assert abs(buf[(p * 4 + i) * 2] - math.cos(ang)) < 1e-7
+            assert abs(buf[(p * 4 + i) * 2 + 1] - math.sin(ang)) < 1e-7
+    assert _lib.load().fp4kv_rope_table(buf, 6, 7, 10000.0) == -1

@@ -1,0 +1,165 @@
+"""GPU parity of fp4kv_attention_chunk (with fp4kv_rope_rel on the queries
+and fp4kv_quantize_append filling the cache) against the float64 oracle.
+
+Bar: max-abs error <= 1e-2 and mean-abs error <= 1e-3 of the float32-output
+kernel against the oracle on the same decoded cache (the cache bytes
+themselves are checked bit-exact on the way).  Full-size workloads compare
+sampled query rows the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+from fp4_kv_cache_fp4kv_amd import workloads as wl
+from oracle.stream import OracleCache
+from streams import (compare_cache, device_tensor, err_stats, gpu_cache, say, shots_of,
+                     step_inputs)
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS = 1e-2, 1e-3
+
+
+def _gpu_step(api, gc, w, c, q, qb, k, kb, v, vb, out_dtype=torch.float32, append=True):
+    f0, n = w.chunk_frames(c)
+    shots = shots_of(w, f0, n)
+    if append:
+        api.quantize_append(gc, device_tensor(k, kb), device_tensor(v, vb), f0, n, shots)
+    pos0 = api.cache_positions(w.S, w.W, f0, n)
+    qr = api.rope_rel(device_tensor(q, qb), pos0, w.T, gc.cos_sin, rot_dim=gc.rot_dim)
+    o = api.attention_chunk(gc, qr, f0, n, shots, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy()
+
+
+def _run_stream(w, steps, rows=None, heads=None, check_every=True, rot_dim=None):
+    from fp4_kv_cache_fp4kv_amd import api
+    gc, oc = gpu_cache(w, rot_dim), OracleCache.for_workload(w, rot_dim)
+    results = []
+    checks = sorted(steps)
+    for c in range(max(steps) + 1):
+        f0, n = w.chunk_frames(c)
+        (q, qb), (k, kb), (v, vb) = step_inputs(w, c)
+        shots = shots_of(w, f0, n)
+        # the oracle skips chunks that are evicted before the next checked
+        # step (every slot then holds a frame it did append)
+        nxt = min(x for x in checks if x >= c)
+        f1_next = sum(w.chunk_frames(nxt))
+        if f0 < w.S or f0 + n > f1_next - w.W:
+            oc.append(k, v, f0, n, shots)
+        say(f"attention {w.name} step {c} frames {f0}..{f0 + n - 1}")
+        got = _gpu_step(api, gc, w, c, q, qb, k, kb, v, vb)
+        if c not in steps:
+            continue
+        assert not compare_cache(gc, oc), (w.name, c)
+        r = np.arange(n * w.T) if rows is None else np.asarray([x for x in rows if x < n * w.T])
+        hs = list(range(w.H)) if heads is None else heads
+        ref = oc.attention(q, f0, n, shots, rows=r, heads=hs)
+        mx, mn = err_stats(got[r][:, hs], ref)
+        say(f"  max-abs {mx:.3e} mean-abs {mn:.3e}")
+        results.append((c, mx, mn))
+        assert mx <= MAX_ABS and mn <= MEAN_ABS, (w.name, c, mx, mn)
+    return results
+
+
+def test_attention_tiny_stream():
+    _run_stream(wl.TINY, list(range(wl.TINY.n_chunks)))
+
+
+def test_attention_tiny_partial_rope():
+    _run_stream(wl.TINY, [0, 3, 5], rot_dim=32)
+
+
+def test_attention_multishot_stride2_partial_chunk():
+    w = wl.Workload("tiny_mix", H=3, D=64, T=24, C=3, S=2, W=6, n_frames=20, seed=21,
+                    dtype="bf16", token_stride=2, shot_len=5)
+    _run_stream(w, list(range(w.n_chunks)))
+
+
+def test_attention_d128_ragged_tiles():
+    # T = 100 tokens: 2 tiles per frame, the second ragged; Nq = 300 rows
+    w = wl.Workload("d128", H=2, D=128, T=100, C=3, S=1, W=6, n_frames=15, seed=22,
+                    outlier_p=0.01, outlier_scale=20.0)
+    _run_stream(w, [0, 1, 2, 4])
+
+
+def test_attention_all_frames_block_causal_in_one_call():
+    """With nothing evicted, one call over every frame (block-causal mask in
+    the kernel) equals the oracle over all frames."""
+    from fp4_kv_cache_fp4kv_amd import api
+    w = wl.Workload("dense", H=2, D=64, T=16, C=2, S=1, W=12, n_frames=12, seed=23, dtype="f32")
+    gc, oc = gpu_cache(w), OracleCache.for_workload(w)
+    qs = []
+    for c in range(w.n_chunks):
+        f0, n = w.chunk_frames(c)
+        (q, _), (k, kb), (v, vb) = step_inputs(w, c)
+        api.quantize_append(gc, device_tensor(k, kb), device_tensor(v, vb), f0, n, [0] * n)
+        oc.append(k, v, f0, n, [0] * n)
+        qs.append(q)
+    q = np.concatenate(qs)
+    F = w.n_frames
+    say("attention dense all-frames call")
+    qr = api.rope_rel(device_tensor(q, None), 0, w.T, gc.cos_sin)
+    o = api.attention_chunk(gc, qr, 0, F, [0] * F, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oc.attention(q, 0, F, [0] * F)
+    mx, mn = err_stats(o.cpu().numpy(), ref)
+    assert mx <= MAX_ABS and mn <= MEAN_ABS, (mx, mn)
+
+
+def test_attention_bf16_output_and_determinism():
+    from fp4_kv_cache_fp4kv_amd import api
+    w = wl.TINY
+    gc, oc = gpu_cache(w), OracleCache.for_workload(w)
+    for c in range(4):
+        f0, n = w.chunk_frames(c)
+        (q, qb), (k, kb), (v, vb) = step_inputs(w, c)
+        oc.append(k, v, f0, n, [0] * n)
+        o32 = _gpu_step(api, gc, w, c, q, qb, k, kb, v, vb)
+        o16 = _gpu_step(api, gc, w, c, q, qb, k, kb, v, vb, out_dtype=torch.bfloat16, append=False)
+        o16b = _gpu_step(api, gc, w, c, q, qb, k, kb, v, vb, out_dtype=torch.bfloat16,
+                         append=False)
+        assert np.array_equal(o16, o16b)
+        # bf16 output = float32 output rounded once
+        assert np.all(np.abs(o16 - o32) <= np.abs(o32) * 2.0 ** -8 + 1e-30)
+        ref = oc.attention(q, f0, n, [0] * n)
+        mx, mn = err_stats(o16, ref)
+        assert mx <= MAX_ABS and mn <= MEAN_ABS
+
+
+def test_attention_empty_cache_gives_zeros():
+    from fp4_kv_cache_fp4kv_amd import api
+    w = wl.TINY
+    gc = gpu_cache(w)
+    q = torch.randn(2 * w.T, w.H, w.D, device="cuda:0").bfloat16()
+    o = api.attention_chunk(gc, q, 0, 2, [0, 0], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o).item() == 0
+
+
+_FULL_ROWS = None
+
+
+def _sample_rows(w, n_rows=48, seed=0):
+    rng = np.random.default_rng(seed)
+    nq = w.C * w.T
+    edge = [0, 1, 127, 128, 255, w.T - 1, w.T, nq - 129, nq - 128, nq - 1]
+    return np.unique(np.concatenate([edge, rng.integers(0, nq, n_rows)]))
+
+
+@pytest.mark.parametrize("name", ["l13b", "l5b"])
+def test_attention_full_size_sampled(name):
+    w = wl.WORKLOADS[name]
+    steady = (w.S + w.W) // w.C          # first step with a full window
+    steps = [0, steady - 1] if name == "l13b" else [0, steady, steady + 3]
+    _run_stream(w, steps, rows=_sample_rows(w), heads=[0, w.H // 2, w.H - 1])
+
+
+def test_attention_multishot_full_size_sampled():
+    w = wl.L5B_SHOTS
+    # step 6 holds frames 18..20 (the shot boundary cuts the chunk); step 26 is partial
+    _run_stream(w, [6, 7, 26], rows=_sample_rows(w, seed=1), heads=[0, w.H - 1])
+
+
+def test_attention_long_stream_sampled_steps():
+    w = wl.LONG
+    _run_stream(w, [0, 8, 9], rows=_sample_rows(w, seed=2), heads=[1, w.H - 2])
