@@ -96,41 +96,43 @@ struct Raw {
   uint4 vs;        // the 16 tokens' scales of that value block
 };
 
-template <int D>
-struct TileCtx {
-  const AttnParams &p;
-  long long k_row0;    // first key row of the head
-  long long v_row0;    // first value dimension row of the head
-  long long vs_row0;   // first value scale row of the head
-};
-
+// Loads are unconditional (addresses clamped into the frame, results
+// zeroed afterwards) so the compiler keeps them in flight across the compute
+// of the current tile instead of waiting at a branch.
 template <int D>
 __device__ __forceinline__ void load_tile(const AttnParams &p, int head, int slot, int k0,
                                           int nval, Raw &r) {
   const int tid = threadIdx.x;
-  // keys: unit (key, 32 dims)
   constexpr int KU = D / 32;
-  const int key = tid / KU, qd = tid % KU;
-  r.kc = make_uint4(0, 0, 0, 0);
-  r.ks = 0;
-  if (tid < kBN * KU && key < nval) {
-    const long long row = ((long long)head * p.n_slots + slot) * p.Tc + k0 + key;
-    r.kc = *(const uint4 *)(p.k_codes + row * (D / 2) + 16 * qd);
-    r.ks = *(const uint16_t *)(p.k_scales + row * (D / 16) + 2 * qd);
+  if (tid < kBN * KU) {   // all threads for D = 128
+    const int key = tid / KU, qd = tid % KU;
+    const bool ok = key < nval;
+    const long long row = ((long long)head * p.n_slots + slot) * p.Tc + k0 + (ok ? key : 0);
+    const uint4 kc = *(const uint4 *)(p.k_codes + row * (D / 2) + 16 * qd);
+    const uint32_t ks = *(const uint16_t *)(p.k_scales + row * (D / 16) + 2 * qd);
+    r.kc = ok ? kc : make_uint4(0, 0, 0, 0);
+    r.ks = ok ? ks : 0u;
   }
-  // values: unit (2 dimension rows, 16 tokens)
-  const int rp = tid >> 2, kg = tid & 3;
-  r.vc[0] = r.vc[1] = make_uint2(0, 0);
-  r.vs = make_uint4(0, 0, 0, 0);
-  const int tok = k0 + 16 * kg;
-  if (tid < 2 * D && tok < p.Tv) {
+  if (tid < 2 * D) {
+    const int rp = tid >> 2, kg = tid & 3;
+    const int tok = k0 + 16 * kg;
+    const bool ok = tok < p.Tv;
+    const int tk = ok ? tok : 0;
     const long long drow = ((long long)head * p.n_slots + slot) * D + 2 * rp;
-    r.vc[0] = *(const uint2 *)(p.v_codes + drow * (p.Tv / 2) + tok / 2);
-    r.vc[1] = *(const uint2 *)(p.v_codes + (drow + 1) * (p.Tv / 2) + tok / 2);
+    const uint2 c0 = *(const uint2 *)(p.v_codes + drow * (p.Tv / 2) + tk / 2);
+    const uint2 c1 = *(const uint2 *)(p.v_codes + (drow + 1) * (p.Tv / 2) + tk / 2);
     const long long srow = ((long long)head * p.n_slots + slot) * (D / 16) + (2 * rp) / 16;
-    r.vs = *(const uint4 *)(p.v_scales + srow * p.Tv + tok);
+    const uint4 vs = *(const uint4 *)(p.v_scales + srow * p.Tv + tk);
+    r.vc[0] = ok ? c0 : make_uint2(0, 0);
+    r.vc[1] = ok ? c1 : make_uint2(0, 0);
+    r.vs = ok ? vs : make_uint4(0, 0, 0, 0);
   }
 }
+
+// Physical LDS row of key k in a K tile: rows 8..15 of every 16 swap their
+// halves, so the 8 lanes that read together (keys {0-3, 8-11} + 16j and
+// {4-7, 12-15} + 16j under sigma) hit 8 different bank groups.
+__device__ __forceinline__ int krow_phys(int k) { return k ^ (((k >> 3) & 1) << 2); }
 
 template <int D>
 __device__ __forceinline__ void dequant_tile(const Raw &r, int nval, Smem<D> &sm, int buf) {
@@ -152,7 +154,7 @@ __device__ __forceinline__ void dequant_tile(const Raw &r, int nval, Smem<D> &sm
     }
     // rows past the end of the frame were not loaded: they hold zeros, and
     // zero codes decode to zero
-    uint4 *dst = (uint4 *)&sm.kh[buf][key][32 * qd];
+    uint4 *dst = (uint4 *)&sm.kh[buf][krow_phys(key)][32 * qd];
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
   }
@@ -193,6 +195,12 @@ __device__ __forceinline__ void dequant_tile(const Raw &r, int nval, Smem<D> &sm
 
 template <int D>
 __host__ __device__ constexpr size_t smem_bytes() { return sizeof(Smem<D>); }
+
+// Softmax rescaling is lazy: the reference maximum of a row moves only when
+// a score exceeds it by more than 2^kTau (log2 units), so weights stay below
+// 2^kTau (representable in f16) and the output accumulators are rescaled
+// rarely.
+constexpr float kTau = 8.0f;
 
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
@@ -248,59 +256,52 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
 
   const int n_fl = sm.n_fl;
   const int n_tiles = (p.Tc + kBN - 1) / kBN;
-  const int total = n_fl * n_tiles;
+  const int last_nval = p.Tc - (n_tiles - 1) * kBN;
 
   f32x16 oacc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b)
 #pragma unroll
     for (int j = 0; j < 16; ++j) oacc[b][j] = 0.0f;
-  float m_run = -1.0e30f, l_part = 0.0f, gv_cur = 1.0f, cf = 0.0f;
-  bool lane_vis = false, wave_any = false;
-  f16x8 qhi[KS], qlo[KS];
+  float m_run = -1.0e30f, l_part = 0.0f, gv_cur = 1.0f;
   const int half_rot = p.rot_dim >> 1;
+  const int krow = krow_phys(sigma(n));   // + 32 b for key block b
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
   Raw raw;
-  if (total > 0) {
-    load_tile<D>(p, head, sm.fl_slot[0], 0, min(kBN, p.Tc), raw);
-    dequant_tile<D>(raw, min(kBN, p.Tc), sm, 0);
+  int buf = 0;
+  if (n_fl > 0) {
+    const int nv0 = n_tiles == 1 ? last_nval : kBN;
+    load_tile<D>(p, head, sm.fl_slot[0], 0, nv0, raw);
+    dequant_tile<D>(raw, nv0, sm, 0);
   }
   __syncthreads();
 
-  for (int it = 0; it < total; ++it) {
-    const int fi = it / n_tiles;
-    const int t = it - fi * n_tiles;
-    const int nval = min(kBN, p.Tc - t * kBN);
-    const int buf = it & 1;
-    int nval_next = 0;
-    if (it + 1 < total) {
-      const int fn = (it + 1) / n_tiles, tn = (it + 1) - fn * n_tiles;
-      nval_next = min(kBN, p.Tc - tn * kBN);
-      load_tile<D>(p, head, sm.fl_slot[fn], tn * kBN, nval_next, raw);
-    }
-
-    if (t == 0) {
-      // ---- new key frame: visibility, tensor scales, turned-back queries
-      const int kf = sm.fl_kf[fi], pos = sm.fl_pos[fi];
-      const float gv = sm.fl_gv[fi];
-      lane_vis = row_ok && (kf / p.C <= my_qchunk) && (kf < p.S || sm.fl_shot[fi] == my_qshot);
-      wave_any = __ballot(lane_vis) != 0ull;
-      const float ratio = fi == 0 ? 1.0f : __fdiv_rn(gv_cur, gv);
-      gv_cur = gv;
+  for (int fi = 0; fi < n_fl; ++fi) {
+    // ---- new key frame: visibility, tensor scales, turned-back queries
+    const int kf = sm.fl_kf[fi], pos = sm.fl_pos[fi];
+    const float gv = sm.fl_gv[fi];
+    const bool lane_vis =
+        row_ok && (kf / p.C <= my_qchunk) && (kf < p.S || sm.fl_shot[fi] == my_qshot);
+    const bool wave_any = __ballot(lane_vis) != 0ull;
+    const bool wave_all = __ballot(lane_vis) == ~0ull;
+    if (fi > 0) {   // keep O = g_v * acc across the change of tensor scale
+      const float ratio = __fdiv_rn(gv_cur, gv);
 #pragma unroll
       for (int b = 0; b < DB; ++b)
 #pragma unroll
         for (int j = 0; j < 16; ++j) oacc[b][j] *= ratio;
-      cf = p.scale_log2 * sm.fl_gk[fi];
+    }
+    gv_cur = gv;
+    const float cf = p.scale_log2 * sm.fl_gk[fi];
+    f16x8 qhi[KS], qlo[KS];
+    {
       const float *tab = p.cos_sin + (long long)pos * p.rot_dim;
       const long long qoff = ((long long)(row_ok ? my_row : 0) * p.H + head) * D + 8 * hf;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         float x[8];
-        if (!row_ok) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = 0.0f;
-        } else if (p.q_f32) {
+        if (p.q_f32) {
           const float4 a = *(const float4 *)((const float *)p.q + qoff + 16 * kk);
           const float4 b = *(const float4 *)((const float *)p.q + qoff + 16 * kk + 4);
           x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
@@ -318,10 +319,10 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int pair = 8 * kk + 4 * hf + e;
-          float ra = x[2 * e], rb = x[2 * e + 1];
+          float ra = row_ok ? x[2 * e] : 0.0f, rb = row_ok ? x[2 * e + 1] : 0.0f;
           if (pair < half_rot) {
             const float2 cs = *(const float2 *)(tab + 2 * pair);
-            rotate_pair(x[2 * e], x[2 * e + 1], cs.x, -cs.y, ra, rb);
+            rotate_pair(ra, rb, cs.x, -cs.y, ra, rb);
           }
           const f16x2 h2 = {(_Float16)ra, (_Float16)rb};
           const f16x2 l2 = {(_Float16)(ra - (float)h2[0]), (_Float16)(rb - (float)h2[1])};
@@ -333,71 +334,91 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
       }
     }
 
-    if (wave_any) {
-      // ---- S^T = K (Q_hi + Q_lo)^T for 2 blocks of 32 keys
-      f32x16 sacc[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[b][j] = 0.0f;
-        const int krow = 32 * b + sigma(n);
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const f16x8 a = as_f16x8(*(const uint4 *)&sm.kh[buf][krow][16 * kk + 8 * hf]);
-          sacc[b] = mfma32(a, qhi[kk], sacc[b]);
-          sacc[b] = mfma32(a, qlo[kk], sacc[b]);
-        }
+    for (int t = 0; t < n_tiles; ++t) {
+      const int nval = t == n_tiles - 1 ? last_nval : kBN;
+      // ---- prefetch the next tile's packed codes and scales
+      const bool has_next = t + 1 < n_tiles || fi + 1 < n_fl;
+      int nval_next = 0;
+      if (has_next) {
+        const bool same = t + 1 < n_tiles;
+        const int tn = same ? t + 1 : 0;
+        nval_next = tn == n_tiles - 1 ? last_nval : kBN;
+        load_tile<D>(p, head, sm.fl_slot[same ? fi : fi + 1], tn * kBN, nval_next, raw);
       }
-      // ---- mask and online softmax; exp2 argument = s * cf - m
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = 32 * b + 16 * (j >> 3) + 8 * hf + (j & 7);
-          const float s = (lane_vis && key < nval) ? sacc[b][j] : -INFINITY;
-          sacc[b][j] = s;
-          tmax = fmaxf(tmax, s);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax * cf);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float lsum = 0.0f;
-      f16x8 pb[4];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[b][8 * t2 + 2 * e], cf, -m_new));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[b][8 * t2 + 2 * e + 1], cf, -m_new));
-            lsum += p0 + p1;
-            const f16x2 ph = {(_Float16)p0, (_Float16)p1};
-            w[e] = bits(ph);
-          }
-          pb[2 * b + t2] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
-        }
-      l_part = l_part * alpha + lsum;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[b][j] *= alpha;
-      // ---- O^T += V^T P^T, 4 slices of 16 keys
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const f16x8 a = as_f16x8(*(const uint4 *)&sm.vt[buf][32 * db + n][16 * t4 + 8 * hf]);
-          oacc[db] = mfma32(a, pb[t4], oacc[db]);
-        }
-      }
-    }
 
-    if (it + 1 < total) dequant_tile<D>(raw, nval_next, sm, buf ^ 1);
-    __syncthreads();
+      if (wave_any) {
+        // ---- S^T = K (Q_hi + Q_lo)^T for 2 blocks of 32 keys
+        f32x16 sacc[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) sacc[b][j] = 0.0f;
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) {
+            const f16x8 a = as_f16x8(*(const uint4 *)&sm.kh[buf][32 * b + krow][16 * kk + 8 * hf]);
+            sacc[b] = mfma32(a, qhi[kk], sacc[b]);
+            sacc[b] = mfma32(a, qlo[kk], sacc[b]);
+          }
+        }
+        // ---- mask (tail tiles and rows that do not see this frame)
+        if (!(wave_all && nval == kBN)) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int key = 32 * b + 16 * (j >> 3) + 8 * hf + (j & 7);
+              sacc[b][j] = (lane_vis && key < nval) ? sacc[b][j] : -INFINITY;
+            }
+        }
+        // ---- online softmax, exp2 argument = s * cf - m
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, sacc[b][j]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * cf;
+        const bool grow = tmax > m_run + kTau;
+        if (__ballot(grow) != 0ull) {
+          const float m_new = fmaxf(m_run, tmax);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_part *= alpha;
+#pragma unroll
+          for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) oacc[b][j] *= alpha;
+        }
+        f16x8 pb[4];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[b][8 * t2 + 2 * e], cf, -m_run));
+              const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[b][8 * t2 + 2 * e + 1], cf, -m_run));
+              const f16x2 ph = {(_Float16)p0, (_Float16)p1};
+              l_part = __builtin_amdgcn_fdot2(ph, ones, l_part, false);
+              w[e] = bits(ph);
+            }
+            pb[2 * b + t2] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
+          }
+        // ---- O^T += V^T P^T, 4 slices of 16 keys
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const f16x8 a = as_f16x8(*(const uint4 *)&sm.vt[buf][32 * db + n][16 * t4 + 8 * hf]);
+            oacc[db] = mfma32(a, pb[t4], oacc[db]);
+          }
+        }
+      }
+
+      if (has_next) dequant_tile<D>(raw, nval_next, sm, buf ^ 1);
+      buf ^= 1;
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: O = g_v * acc / l
