@@ -125,9 +125,7 @@ int fp4kv_quantize_append(const fp4kv_cache *c, const void *k, const void *v, in
   p.slot_frame = c->slot_frame;
   p.slot_shot = c->slot_shot;
   p.tscale_in = tscale_in;
-  p.ws_counter = (uint32_t *)((uint8_t *)workspace + kWsCounterOff);
-  p.ws_scale = (float *)((uint8_t *)workspace + kWsScaleOff);
-  p.ws_partial = (uint32_t *)((uint8_t *)workspace + kWsPartialOff);
+  p.ws_partial = (uint32_t *)workspace;
   p.H = c->n_heads;
   p.D = c->head_dim;
   p.T = c->tokens_per_frame;

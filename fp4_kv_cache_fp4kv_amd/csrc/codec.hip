@@ -3,13 +3,10 @@
 // hysenlabs.com, "NVFP4, sequence parallel and the async decode path").
 //
 // Two kernels per call, on the caller's stream:
-//   amax_kernel    grid (kAmaxBlocks, 2): max |x| over the kept tokens of K
-//                  (y = 0) and V (y = 1); the last workgroup to arrive folds
-//                  the partial maxima into g = amax / 2688 and re-zeroes its
-//                  arrival counter.  No workgroup waits for another.
-//   encode_kernel  one thread per 16-element block of one (token, head) row;
-//                  threads are ordered like the cache so each wave writes
-//                  512 contiguous code bytes and 64 contiguous scale bytes.
+//   amax_kernel    grid (kAmaxBlocks, 2): partial max |x| over the kept
+//                  tokens of K (y = 0) and V (y = 1), one per workgroup.
+//   encode_kernel  NVFP4 encode of both tensors straight into their cache
+//                  slots (layouts in include/fp4kv.h), plus the slot metadata.
 #include "fp4kv_device.hpp"
 #include "internal.hpp"
 
@@ -39,70 +36,77 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red) {
 }
 
 // |x| bit patterns compare like the values for non-negative floats, so the
-// maximum is taken on integers: bf16 halves are widened to float32 bits.
-__global__ __launch_bounds__(kThreads) void amax_kernel(AppendParams p) {
-  __shared__ uint32_t red[kThreads / 64];
-  __shared__ int last;
-  const int y = blockIdx.y;
-  const int es = p.in_bf16 ? 2 : 4;
-  const long long row_bytes = (long long)p.H * p.D * es;    // one token, all heads
-  const int chunks_per_row = (int)(row_bytes / 16);
-  const long long n_rows = (long long)p.n_frames * p.Tc;
-  const long long n_chunks = n_rows * chunks_per_row;
-  const uint8_t *base = (const uint8_t *)p.x[y];
-  uint32_t m = 0;
-  for (long long c = (long long)blockIdx.x * kThreads + threadIdx.x; c < n_chunks;
-       c += (long long)gridDim.x * kThreads) {
-    const long long r = c / chunks_per_row;
-    const int within = (int)(c - r * chunks_per_row);
-    const long long frame = r / p.Tc;
-    const long long tc = r - frame * p.Tc;
-    const long long tok = frame * p.T + tc * p.stride;
-    const uint4 v = *(const uint4 *)(base + tok * row_bytes + (long long)within * 16);
+// maximum is taken on integers: bf16 halves with a packed 16-bit max, float32
+// words directly.  Each thread keeps kAmaxUnroll 16-byte loads in flight.
+constexpr int kAmaxUnroll = 4;
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t fold_max(uint32_t m, const uint4 &v, bool bf16) {
+  if (bf16) {
+    u16x2 acc = __builtin_bit_cast(u16x2, m);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (p.in_bf16) {
-        const uint32_t lo = (w[i] & 0x7FFFu) << 16, hi = w[i] & 0x7FFF0000u;
-        m = m > lo ? m : lo;
-        m = m > hi ? m : hi;
-      } else {
-        const uint32_t a = w[i] & 0x7FFFFFFFu;
-        m = m > a ? m : a;
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+    return __builtin_bit_cast(uint32_t, acc);
+  }
+  m = max(m, v.x & 0x7FFFFFFFu);
+  m = max(m, v.y & 0x7FFFFFFFu);
+  m = max(m, v.z & 0x7FFFFFFFu);
+  return max(m, v.w & 0x7FFFFFFFu);
+}
+
+__global__ __launch_bounds__(kThreads) void amax_kernel(AppendParams p) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int y = blockIdx.y;
+  const bool bf16 = p.in_bf16;
+  const uint32_t row_chunks = (uint32_t)(p.H * p.D * (bf16 ? 2 : 4) / 16);  // one token
+  const uint32_t n_chunks = (uint32_t)(p.n_frames * p.Tc) * row_chunks;
+  const uint4 *base = (const uint4 *)p.x[y];
+  const uint32_t step = gridDim.x * kThreads;
+  uint32_t m = 0;
+  for (uint32_t c0 = blockIdx.x * kThreads + threadIdx.x; c0 < n_chunks;
+       c0 += step * kAmaxUnroll) {
+    uint4 v[kAmaxUnroll];
+#pragma unroll
+    for (int k = 0; k < kAmaxUnroll; ++k) {
+      const uint32_t c = c0 + k * step;
+      uint32_t addr = c;
+      if (p.stride != 1) {   // kept token r is stored token r * stride (frames hold T tokens)
+        const uint32_t r = c / row_chunks;
+        const uint32_t frame = r / (uint32_t)p.Tc, tc = r - frame * (uint32_t)p.Tc;
+        addr = (frame * (uint32_t)p.T + tc * (uint32_t)p.stride) * row_chunks + (c - r * row_chunks);
       }
+      v[k] = c < n_chunks ? base[addr] : make_uint4(0, 0, 0, 0);
     }
+#pragma unroll
+    for (int k = 0; k < kAmaxUnroll; ++k) m = fold_max(m, v[k], bf16);
   }
+  if (bf16) m = max(m & 0xFFFFu, m >> 16) << 16;   // bf16 bits -> float32 bits
   m = block_max_u32(m, red);
-  if (threadIdx.x == 0) {
-    __hip_atomic_store(&p.ws_partial[y * kAmaxBlocks + blockIdx.x], m, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    __threadfence();
-    const uint32_t arrived = atomicAdd(&p.ws_counter[y], 1u);
-    last = (arrived == (uint32_t)gridDim.x - 1u);
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  uint32_t mm = 0;
-  for (int i = threadIdx.x; i < (int)gridDim.x; i += kThreads) {
-    const uint32_t v = __hip_atomic_load(&p.ws_partial[y * kAmaxBlocks + i], __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    mm = mm > v ? mm : v;
-  }
-  __syncthreads();  // red[] is reused
-  mm = block_max_u32(mm, red);
-  if (threadIdx.x == 0) {
-    const float amax = __uint_as_float(mm);
-    // g = amax / (6 * 448): the largest block then maps to the largest E4M3
-    // scale.  A tensor of zeros gets g = 1.
-    p.ws_scale[y] = amax > 0.0f ? __fdiv_rn(amax, 2688.0f) : 1.0f;
-    p.ws_counter[y] = 0u;
-  }
+  if (threadIdx.x == 0) p.ws_partial[y * kAmaxBlocks + blockIdx.x] = m;
+}
+
+// Tensor scale g = amax / 2688 from the kAmaxBlocks partial maxima of tensor
+// y (2688 = 6 * 448: the largest block then maps to the largest E4M3 scale;
+// a tensor of zeros gets g = 1).  Every encode workgroup folds the partials
+// itself, so no workgroup waits for another and no atomics are needed.
+__device__ __forceinline__ float tensor_scale(const AppendParams &p, int y, uint32_t *red) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < kAmaxBlocks; i += kThreads)
+    m = max(m, p.ws_partial[y * kAmaxBlocks + i]);
+  m = block_max_u32(m, red);
+  const float amax = __uint_as_float(m);
+  return amax > 0.0f ? __fdiv_rn(amax, 2688.0f) : 1.0f;
 }
 
 // Encode one 16-element block: returns the two packed code words; *scale8
 // receives the E4M3 scale code.  Every step rounds once, in float32, as the
-// format definition states.
+// format definition states.  The element step y = x * r goes through the
+// gfx950 float32 -> E2M1 conversion (scale 1), which rounds to nearest even
+// and saturates exactly like e2m1_encode_mag (checked on every non-NaN
+// float32); the sign of y is the sign of x.  x = 0 keeps its signed zero; a
+// zero block scale zeroes every magnitude.
 __device__ __forceinline__ uint2 encode_block(const float (&x)[16], float g, float d,
                                               uint32_t *scale8) {
   float a = 0.0f;
@@ -112,18 +116,27 @@ __device__ __forceinline__ uint2 encode_block(const float (&x)[16], float g, flo
   const uint32_t s8 = e4m3_encode_sat(s);
   const float sv = e4m3_value(s8);
   const float Sb = sv * g;
-  const float r = __frcp_rn(Sb);
-  uint32_t w[2] = {0u, 0u};
+  float r = __frcp_rn(Sb);
+  r = sv == 0.0f ? 0.0f : r;
+  float y[16];
+  if (__builtin_isinf(r)) {     // block scale below 2^-128: 0 * inf must stay 0
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float ax = fabsf(x[i]);
-    uint32_t m = e2m1_encode_mag(ax * r);
-    m = (sv == 0.0f || ax == 0.0f) ? 0u : m;
-    const uint32_t code = ((__float_as_uint(x[i]) >> 31) << 3) | m;
-    w[i >> 3] |= code << (4 * (i & 7));
+    for (int i = 0; i < 16; ++i) y[i] = x[i] == 0.0f ? x[i] : x[i] * r;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = x[i] * r;
   }
+  uint32_t w0 = 0u, w1 = 0u;
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[0], y[1], 1.0f, 0);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[2], y[3], 1.0f, 1);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[4], y[5], 1.0f, 2);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[6], y[7], 1.0f, 3);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[8], y[9], 1.0f, 0);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[10], y[11], 1.0f, 1);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[12], y[13], 1.0f, 2);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[14], y[15], 1.0f, 3);
   *scale8 = s8;
-  return make_uint2(w[0], w[1]);
+  return make_uint2(w0, w1);
 }
 
 __device__ __forceinline__ void load_block(const AppendParams &p, int y, long long src,
@@ -151,20 +164,22 @@ __device__ __forceinline__ int slot_of(const AppendParams &p, int f) {
   return f < p.S ? f : p.S + (f - p.S) % p.W;
 }
 
-// blockIdx.y = 0: keys, token-major rows.  One thread per (token, 16-block);
-// blocks vary fastest, so a wave reads whole 256-byte rows and writes 512
-// contiguous code bytes.
-// blockIdx.y = 1: values, dimension-major.  One thread per (8 tokens,
-// 16-block); it writes one 4-byte word (8 token nibbles) in each of the
-// block's 16 dimension rows plus 8 scale bytes.  Padding tokens Tc..Tv-1 of
-// the last group are written as zeros.
+// One launch encodes both tensors.  Workgroups [0, p.v_blocks) encode the
+// values, dimension-major: one thread per (8 tokens, 16-block) writes one
+// 4-byte word (8 token nibbles) in each of the block's 16 dimension rows plus
+// 8 scale bytes; padding tokens Tc..Tv-1 of the last group are written as
+// zeros.  They start first because each thread carries 8 blocks.  The other
+// workgroups encode the keys, token-major: one thread per (token, 16-block),
+// blocks fastest, so a wave reads whole rows and writes contiguous bytes.
 __global__ __launch_bounds__(kThreads) void encode_kernel(AppendParams p) {
-  const int y = blockIdx.y;
-  const float g = p.tscale_in ? p.tscale_in[y] : p.ws_scale[y];
-  const float d = 6.0f * g;
   const int nb = p.D >> 4;                                   // blocks per row
+  __shared__ uint32_t red[kThreads / 64];
+  const bool is_v = (int)blockIdx.x < p.v_blocks;
+  const int y = is_v ? 1 : 0;
+  const float g = p.tscale_in ? p.tscale_in[y] : tensor_scale(p, y, red);
+  const float d = 6.0f * g;
 
-  if (blockIdx.x == 0 && threadIdx.x < p.n_frames) {
+  if ((blockIdx.x == 0 || (int)blockIdx.x == p.v_blocks) && threadIdx.x < p.n_frames) {
     const int j = threadIdx.x, f = p.frame0 + j;
     const int slot = slot_of(p, f);
     p.tscale[y][slot] = g;
@@ -174,69 +189,67 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(AppendParams p) {
     }
   }
 
-  if (y == 0) {
-    const long long units = (long long)p.H * p.n_frames * p.Tc * nb;
-    for (long long u = (long long)blockIdx.x * kThreads + threadIdx.x; u < units;
-         u += (long long)gridDim.x * kThreads) {
-      const int b = (int)(u % nb);
-      long long rest = u / nb;
-      const int tc = (int)(rest % p.Tc);
-      rest /= p.Tc;
-      const int j = (int)(rest % p.n_frames);
-      const int h = (int)(rest / p.n_frames);
-      const int slot = slot_of(p, p.frame0 + j);
-      const long long tok = (long long)j * p.T + (long long)tc * p.stride;
-      float x[16];
-      load_block(p, 0, (tok * p.H + h) * p.D + b * 16, x);
-      uint32_t s8;
-      const uint2 packed = encode_block(x, g, d, &s8);
-      const long long row = ((long long)h * p.n_slots + slot) * p.Tc + tc;
-      *(uint2 *)(p.codes[0] + row * (p.D >> 1) + b * 8) = packed;
-      p.scales[0][row * nb + b] = (uint8_t)s8;
-    }
+  if (!is_v) {
+    const uint32_t units = (uint32_t)(p.H * p.n_frames * p.Tc * nb);
+    const uint32_t u = (blockIdx.x - p.v_blocks) * kThreads + threadIdx.x;
+    if (u >= units) return;
+    const int b = (int)(u % nb);
+    uint32_t rest = u / nb;
+    const int tc = (int)(rest % p.Tc);
+    rest /= p.Tc;
+    const int j = (int)(rest % p.n_frames);
+    const int h = (int)(rest / p.n_frames);
+    const int slot = slot_of(p, p.frame0 + j);
+    const long long tok = (long long)j * p.T + (long long)tc * p.stride;
+    float x[16];
+    load_block(p, 0, (tok * p.H + h) * p.D + b * 16, x);
+    uint32_t s8;
+    const uint2 packed = encode_block(x, g, d, &s8);
+    const long long row = ((long long)h * p.n_slots + slot) * p.Tc + tc;
+    *(uint2 *)(p.codes[0] + row * (p.D >> 1) + b * 8) = packed;
+    p.scales[0][row * nb + b] = (uint8_t)s8;
     return;
   }
 
   const int groups = p.Tv >> 3;                              // 8-token groups
-  const long long units = (long long)p.H * p.n_frames * groups * nb;
-  for (long long u = (long long)blockIdx.x * kThreads + threadIdx.x; u < units;
-       u += (long long)gridDim.x * kThreads) {
-    const int b = (int)(u % nb);
-    long long rest = u / nb;
-    const int grp = (int)(rest % groups);
-    rest /= groups;
-    const int j = (int)(rest % p.n_frames);
-    const int h = (int)(rest / p.n_frames);
-    const int slot = slot_of(p, p.frame0 + j);
-    uint32_t rows[16];                                       // one word per dimension
+  const uint32_t units = (uint32_t)(p.H * p.n_frames * groups * nb);
+  const uint32_t u = blockIdx.x * kThreads + threadIdx.x;
+  if (u >= units) return;
+  const int b = (int)(u % nb);
+  uint32_t rest = u / nb;
+  const int grp = (int)(rest % groups);
+  rest /= groups;
+  const int j = (int)(rest % p.n_frames);
+  const int h = (int)(rest / p.n_frames);
+  const int slot = slot_of(p, p.frame0 + j);
+  uint32_t rows[16];                                         // one word per dimension
 #pragma unroll
-    for (int r = 0; r < 16; ++r) rows[r] = 0u;
-    uint32_t sc_lo = 0u, sc_hi = 0u;
+  for (int r = 0; r < 16; ++r) rows[r] = 0u;
+  uint32_t sc_lo = 0u, sc_hi = 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int tc = 8 * grp + i;
-      if (tc < p.Tc) {
-        const long long tok = (long long)j * p.T + (long long)tc * p.stride;
-        float x[16];
-        load_block(p, 1, (tok * p.H + h) * p.D + b * 16, x);
-        uint32_t s8;
-        const uint2 packed = encode_block(x, g, d, &s8);
+  for (int i = 0; i < 8; ++i) {
+    const int tc = 8 * grp + i;
+    if (tc < p.Tc) {
+      const long long tok = (long long)j * p.T + (long long)tc * p.stride;
+      float x[16];
+      load_block(p, 1, (tok * p.H + h) * p.D + b * 16, x);
+      uint32_t s8;
+      const uint2 packed = encode_block(x, g, d, &s8);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t code = ((r < 8 ? packed.x : packed.y) >> (4 * (r & 7))) & 0xFu;
-          rows[r] |= code << (4 * i);
-        }
-        if (i < 4) sc_lo |= s8 << (8 * i);
-        else sc_hi |= s8 << (8 * (i - 4));
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t code = ((r < 8 ? packed.x : packed.y) >> (4 * (r & 7))) & 0xFu;
+        rows[r] |= code << (4 * i);
       }
+      if (i < 4) sc_lo |= s8 << (8 * i);
+      else sc_hi |= s8 << (8 * (i - 4));
     }
-    const long long vrow0 = ((long long)h * p.n_slots + slot) * p.D + 16 * b;
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      *(uint32_t *)(p.codes[1] + (vrow0 + r) * (p.Tv >> 1) + 4 * grp) = rows[r];
-    const long long srow = ((long long)h * p.n_slots + slot) * nb + b;
-    *(uint2 *)(p.scales[1] + srow * p.Tv + 8 * grp) = make_uint2(sc_lo, sc_hi);
   }
+  const long long vrow0 = ((long long)h * p.n_slots + slot) * p.D + 16 * b;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    *(uint32_t *)(p.codes[1] + (vrow0 + r) * (p.Tv >> 1) + 4 * grp) = rows[r];
+  const long long srow = ((long long)h * p.n_slots + slot) * nb + b;
+  *(uint2 *)(p.scales[1] + srow * p.Tv + 8 * grp) = make_uint2(sc_lo, sc_hi);
 }
 
 __global__ void reset_kernel(int32_t *slot_frame, int32_t *slot_shot, float *kt, float *vt, int n) {
@@ -258,19 +271,19 @@ hipError_t launch_cache_reset(const fp4kv_cache &c, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_append(const AppendParams &p, hipStream_t s) {
+hipError_t launch_append(const AppendParams &p_in, hipStream_t s) {
+  AppendParams p = p_in;
+  const long long k_units = (long long)p.H * p.n_frames * p.Tc * (p.D >> 4);
+  const long long v_units = (long long)p.H * p.n_frames * (p.Tv >> 3) * (p.D >> 4);
+  p.v_blocks = (int)((v_units + kThreads - 1) / kThreads);
+  const long long k_blocks = (k_units + kThreads - 1) / kThreads;
   if (!p.tscale_in) {
     hipLaunchKernelGGL(amax_kernel, dim3(kAmaxBlocks, 2), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const long long units = (long long)p.H * p.n_frames * p.Tc * (p.D >> 4);
-  // grid sized for the key pass; the value pass has 8x fewer threads and
-  // strides over the same grid
-  long long blocks = (units + kThreads - 1) / kThreads;
-  if (blocks > 65535) blocks = 65535;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(encode_kernel, dim3((unsigned)blocks, 2), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(encode_kernel, dim3((unsigned)(p.v_blocks + k_blocks)), dim3(kThreads), 0, s,
+                     p);
   return hipGetLastError();
 }
 

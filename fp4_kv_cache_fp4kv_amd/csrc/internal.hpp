@@ -9,16 +9,11 @@
 namespace fp4kv {
 
 // Number of partial maxima per tensor in the append workspace.
-constexpr int kAmaxBlocks = 512;
+constexpr int kAmaxBlocks = 256;
 
-// Workspace layout of fp4kv_quantize_append (bytes from the base):
-//   [0, 8)      uint32 arrival counters for K and V (zero between calls)
-//   [16, 24)    float tensor scales g_k, g_v computed by the amax pass
-//   [64, ...)   uint32 partial maxima [2][kAmaxBlocks]
-constexpr size_t kWsCounterOff = 0;
-constexpr size_t kWsScaleOff = 16;
-constexpr size_t kWsPartialOff = 64;
-constexpr size_t kWsBytes = kWsPartialOff + 2 * kAmaxBlocks * sizeof(uint32_t);
+// Workspace of fp4kv_quantize_append: uint32 partial maxima [2][kAmaxBlocks]
+// (float32 bit patterns of max |x| per workgroup of the amax pass).
+constexpr size_t kWsBytes = 2 * kAmaxBlocks * sizeof(uint32_t);
 
 struct AppendParams {
   const void *x[2];        // K, V inputs [n_frames*T][H][D]
@@ -27,11 +22,10 @@ struct AppendParams {
   float *tscale[2];
   int32_t *slot_frame, *slot_shot;
   const float *tscale_in;  // device [2] or null
-  uint32_t *ws_counter;    // [2]
-  float *ws_scale;         // [2]
   uint32_t *ws_partial;    // [2][kAmaxBlocks]
   int H, D, T, stride, Tc, Tv, S, W, n_slots, frame0, n_frames;
   int in_bf16;
+  int v_blocks;            // workgroups of the value pass in encode_kernel
   int32_t shot[FP4KV_MAX_FRAMES];
 };
 

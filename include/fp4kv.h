@@ -155,8 +155,8 @@ size_t fp4kv_append_workspace_bytes(void);
  *               > 0), or NULL to compute g = amax / 2688 over the kept tokens
  *               of each of K and V (g = 1 when amax = 0).
  *   workspace   device, fp4kv_append_workspace_bytes() bytes, 16-byte
- *               aligned.  It must be zero-filled before its first use; every
- *               call leaves it zero-filled again.  Calls that overlap in time
+ *               aligned, no initialization needed (it holds partial maxima
+ *               between the call's two kernels).  Calls that overlap in time
  *               must use different workspaces.
  *
  * Encoding, per 16-element block b along D of one (token, head) row, all in
