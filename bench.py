@@ -43,7 +43,28 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (5 times), to calibrate the "
+                         "FETCH_SIZE / WRITE_SIZE counters, and exit")
     return ap.parse_args()
+
+
+def attention_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("attention.hip", "fp4kv_device.hpp", "internal.hpp"):
+        h.update(open(os.path.join(ROOT, "fp4_kv_cache_fp4kv_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration(nbytes):
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": src.numel() * 4, "launches": 5}), flush=True)
 
 
 def workload_desc(w):
@@ -95,6 +116,9 @@ def cpu_baseline(w):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by head or by time, see the design notes)", file=sys.stderr)
@@ -173,10 +197,12 @@ def main():
     codec_bytes = kept * es + kept * (0.5 + 1.0 / 16.0)
     codec_gbs = codec_bytes / (codec_ms * 1e-3) / 1e9
 
+    # HBM bytes per attention launch from rocprofv3 counters, valid only for
+    # the kernel source they were taken on
     traffic = None
     try:
         tj = json.load(open(args.traffic_json))
-        if tj.get("workload") == w.name:
+        if tj.get("workload") == w.name and tj.get("source_hash") == attention_source_hash():
             traffic = tj.get("attention_bytes_per_launch")
     except (OSError, ValueError):
         pass
