@@ -47,6 +47,7 @@ constexpr int kBN = 64;    // keys per tile
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kPad = 8;    // f16 elements of padding per LDS row
+constexpr int kXcds = 8;   // accelerator complex dies of MI355X
 
 __device__ __forceinline__ f16x8 as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ uint32_t bits(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
@@ -212,11 +213,19 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, hf = lane >> 5;
-  const int head = blockIdx.y;
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+  // L2).  Give XCD x the contiguous work items [x*per, (x+1)*per) in
+  // head-major order, so each head's FP4 KV is read into few L2s.
+  const int n_qt = (p.Nq + kBM - 1) / kBM;
+  const int n_work = n_qt * p.H;
+  const int per = (n_work + kXcds - 1) / kXcds;
+  const int work = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+  if (work >= n_work) return;
+  const int head = work / n_qt;
   const int f1 = p.q_frame0 + p.n_q_frames;
   const int ws = max(p.S, f1 - p.W);
 
-  const int wg_row0 = blockIdx.x * kBM;
+  const int wg_row0 = (work - head * n_qt) * kBM;
   const int my_row = wg_row0 + wave * 32 + n;
   const bool row_ok = my_row < p.Nq;
   const int my_qf = p.q_frame0 + (row_ok ? my_row : p.Nq - 1) / p.T;
@@ -267,6 +276,9 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
   const int half_rot = p.rot_dim >> 1;
   const int krow = krow_phys(sigma(n));   // + 32 b for key block b
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  const long long qoff = ((long long)(row_ok ? my_row : 0) * p.H + head) * D + 8 * hf;
+  f16x8 qhi[KS], qlo[KS];
+  int prev_pos = 0;
 
   Raw raw;
   int buf = 0;
@@ -294,35 +306,45 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
     }
     gv_cur = gv;
     const float cf = p.scale_log2 * sm.fl_gk[fi];
-    f16x8 qhi[KS], qlo[KS];
+    // Queries turned back by -pos(kf) as f16 hi + lo.  The first frame reads
+    // the rotated queries; later frames turn the previous frame's queries by
+    // -(pos(kf) - pos(prev)), so the queries are read from memory once.
     {
-      const float *tab = p.cos_sin + (long long)pos * p.rot_dim;
-      const long long qoff = ((long long)(row_ok ? my_row : 0) * p.H + head) * D + 8 * hf;
+      const int dpos = fi == 0 ? pos : pos - prev_pos;
+      const float sgn = dpos >= 0 ? -1.0f : 1.0f;   // R(-dpos) = (c, -s) of |dpos|
+      const float *tab = p.cos_sin + (long long)abs(dpos) * p.rot_dim;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         float x[8];
-        if (p.q_f32) {
-          const float4 a = *(const float4 *)((const float *)p.q + qoff + 16 * kk);
-          const float4 b = *(const float4 *)((const float *)p.q + qoff + 16 * kk + 4);
-          x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-          x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-        } else {
-          const uint4 v = *(const uint4 *)((const uint16_t *)p.q + qoff + 16 * kk);
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        if (fi == 0) {
+          if (p.q_f32) {
+            const float4 a = *(const float4 *)((const float *)p.q + qoff + 16 * kk);
+            const float4 b = *(const float4 *)((const float *)p.q + qoff + 16 * kk + 4);
+            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+            x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+          } else {
+            const uint4 v = *(const uint4 *)((const uint16_t *)p.q + qoff + 16 * kk);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[2 * e] = __uint_as_float(w[e] << 16);
-            x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+            for (int e = 0; e < 4; ++e) {
+              x[2 * e] = __uint_as_float(w[e] << 16);
+              x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+            }
           }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = row_ok ? x[e] : 0.0f;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = (float)qhi[kk][e] + (float)qlo[kk][e];
         }
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int pair = 8 * kk + 4 * hf + e;
-          float ra = row_ok ? x[2 * e] : 0.0f, rb = row_ok ? x[2 * e + 1] : 0.0f;
+          float ra = x[2 * e], rb = x[2 * e + 1];
           if (pair < half_rot) {
             const float2 cs = *(const float2 *)(tab + 2 * pair);
-            rotate_pair(ra, rb, cs.x, -cs.y, ra, rb);
+            rotate_pair(x[2 * e], x[2 * e + 1], cs.x, sgn * cs.y, ra, rb);
           }
           const f16x2 h2 = {(_Float16)ra, (_Float16)rb};
           const f16x2 l2 = {(_Float16)(ra - (float)h2[0]), (_Float16)(rb - (float)h2[1])};
@@ -333,6 +355,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
         qlo[kk] = as_f16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
     }
+    prev_pos = pos;
 
     for (int t = 0; t < n_tiles; ++t) {
       const int nval = t == n_tiles - 1 ? last_nval : kBN;
@@ -348,16 +371,30 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
 
       if (wave_any) {
         // ---- S^T = K (Q_hi + Q_lo)^T for 2 blocks of 32 keys
+        // all K operands of a key block are read before its MFMAs, the second
+        // block's reads overlapping the first block's MFMAs
         f32x16 sacc[2];
+        f16x8 ka[2][KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          ka[0][kk] = as_f16x8(*(const uint4 *)&sm.kh[buf][krow][16 * kk + 8 * hf]);
+        __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
 #pragma unroll
           for (int j = 0; j < 16; ++j) sacc[b][j] = 0.0f;
 #pragma unroll
           for (int kk = 0; kk < KS; ++kk) {
-            const f16x8 a = as_f16x8(*(const uint4 *)&sm.kh[buf][32 * b + krow][16 * kk + 8 * hf]);
-            sacc[b] = mfma32(a, qhi[kk], sacc[b]);
-            sacc[b] = mfma32(a, qlo[kk], sacc[b]);
+            if (b == 0)
+              ka[1][kk] = as_f16x8(*(const uint4 *)&sm.kh[buf][32 + krow][16 * kk + 8 * hf]);
+            sacc[b] = mfma32(ka[b][kk], qhi[kk], sacc[b]);
+            sacc[b] = mfma32(ka[b][kk], qlo[kk], sacc[b]);
+            if (b == 0) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            } else {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
           }
         }
         // ---- mask (tail tiles and rows that do not see this frame)
@@ -405,12 +442,26 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
             pb[2 * b + t2] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
           }
         // ---- O^T += V^T P^T, 4 slices of 16 keys
+        // V operands are read DB ahead of their MFMA
+        f16x8 va[4][DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          va[0][db] = as_f16x8(*(const uint4 *)&sm.vt[buf][32 * db + n][8 * hf]);
+        __builtin_amdgcn_sched_group_barrier(0x100, DB, 0);
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const f16x8 a = as_f16x8(*(const uint4 *)&sm.vt[buf][32 * db + n][16 * t4 + 8 * hf]);
-            oacc[db] = mfma32(a, pb[t4], oacc[db]);
+            if (t4 + 1 < 4)
+              va[t4 + 1][db] =
+                  as_f16x8(*(const uint4 *)&sm.vt[buf][32 * db + n][16 * (t4 + 1) + 8 * hf]);
+            oacc[db] = mfma32(va[t4][db], pb[t4], oacc[db]);
+            if (t4 + 1 < 4) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            } else {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
           }
         }
       }
@@ -450,7 +501,8 @@ hipError_t launch_one(const AttnParams &p, hipStream_t s) {
       (const void *)attention_kernel<D, OUT_F32>, hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)bytes);
   if (attr != hipSuccess) return attr;
-  const dim3 grid((p.Nq + kBM - 1) / kBM, p.H);
+  const int n_work = (p.Nq + kBM - 1) / kBM * p.H;
+  const dim3 grid((n_work + kXcds - 1) / kXcds * kXcds);
   hipLaunchKernelGGL((attention_kernel<D, OUT_F32>), grid, dim3(kThreads), bytes, s, p);
   return hipGetLastError();
 }
