@@ -67,6 +67,21 @@ __device__ __forceinline__ f16x2 fp8x2(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
 }
 
+// Lanes i and i + 32 hold two halves of one query row.  gfx950's
+// v_permlane32_swap (a VALU exchange of the two 32-lane halves, no LDS trip)
+// applied to (x, x) returns the low half's values in every lane and the high
+// half's values in every lane; max and sum are symmetric in the two.
+__device__ __forceinline__ float halves_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Key (within a 32-key block) that row m of the S^T operand reads.  With
 // this order the 8 consecutive score registers 8t'..8t'+7 of a lane hold 8
 // consecutive keys, which is what the P^T operand of the PV product needs.
@@ -371,32 +386,27 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
 
       if (wave_any) {
         // ---- S^T = K (Q_hi + Q_lo)^T for 2 blocks of 32 keys
-        // all K operands of a key block are read before its MFMAs, the second
-        // block's reads overlapping the first block's MFMAs
+        // all 16 K operands are read first; the MFMAs then alternate between
+        // the two key blocks so consecutive MFMAs never share an accumulator
         f32x16 sacc[2];
         f16x8 ka[2][KS];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-          ka[0][kk] = as_f16x8(*(const uint4 *)&sm.kh[buf][krow][16 * kk + 8 * hf]);
-        __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+          for (int kk = 0; kk < KS; ++kk)
+            ka[b][kk] = as_f16x8(*(const uint4 *)&sm.kh[buf][32 * b + krow][16 * kk + 8 * hf]);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int j = 0; j < 16; ++j) sacc[b][j] = 0.0f;
 #pragma unroll
-          for (int kk = 0; kk < KS; ++kk) {
-            if (b == 0)
-              ka[1][kk] = as_f16x8(*(const uint4 *)&sm.kh[buf][32 + krow][16 * kk + 8 * hf]);
-            sacc[b] = mfma32(ka[b][kk], qhi[kk], sacc[b]);
-            sacc[b] = mfma32(ka[b][kk], qlo[kk], sacc[b]);
-            if (b == 0) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            } else {
-              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            }
-          }
+        for (int kk = 0; kk < KS; ++kk) {
+          sacc[0] = mfma32(ka[0][kk], qhi[kk], sacc[0]);
+          sacc[1] = mfma32(ka[1][kk], qhi[kk], sacc[1]);
+          sacc[0] = mfma32(ka[0][kk], qlo[kk], sacc[0]);
+          sacc[1] = mfma32(ka[1][kk], qlo[kk], sacc[1]);
         }
+        __builtin_amdgcn_s_setprio(0);
         // ---- mask (tail tiles and rows that do not see this frame)
         if (!(wave_all && nval == kBN)) {
 #pragma unroll
@@ -413,7 +423,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, sacc[b][j]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * cf;
+        tmax = halves_max(tmax) * cf;
         const bool grow = tmax > m_run + kTau;
         if (__ballot(grow) != 0ull) {
           const float m_new = fmaxf(m_run, tmax);
@@ -443,6 +453,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
           }
         // ---- O^T += V^T P^T, 4 slices of 16 keys
         // V operands are read DB ahead of their MFMA
+        __builtin_amdgcn_s_setprio(1);
         f16x8 va[4][DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -464,6 +475,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
             }
           }
         }
+        __builtin_amdgcn_s_setprio(0);
       }
 
       if (has_next) dequant_tile<D>(raw, nval_next, sm, buf ^ 1);
@@ -473,7 +485,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
   }
 
   // ---- epilogue: O = g_v * acc / l
-  const float l = l_part + __shfl_xor(l_part, 32, 64);
+  const float l = halves_sum(l_part);
   const float inv = l > 0.0f ? __fdiv_rn(gv_cur, l) : 0.0f;
   if (!row_ok) return;
   const long long obase = ((long long)my_row * p.H + head) * D;
