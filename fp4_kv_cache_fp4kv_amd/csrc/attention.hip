@@ -7,24 +7,32 @@
 // together ...").
 //
 // Work layout (gfx950, wave64, MFMA 32x32x16 with f16 operands, f32 accum):
-//   * one workgroup = 128 query rows of one head, 4 waves x 32 rows;
-//   * the keys of every visible frame are walked in tiles of 64.  The packed
-//     FP4 codes and E4M3 scales of tile i+1 are loaded into registers while
-//     tile i is computed, then dequantized once per workgroup into a second
-//     LDS buffer (one barrier per tile).  Dequantization is exact: E2M1 x E4M3
-//     has at most 6 significant bits and lies in [2^-10, 2688], so it fits
-//     f16; the hardware converts two FP4 codes to f16 (scale 1) and one packed
-//     f16 multiply applies the block scale;
+//   * one workgroup = 128 query rows of one head, 4 waves x 32 rows, one
+//     workgroup per CU, so every wave owns a SIMD and up to 512 registers;
+//   * the keys of all visible frames are walked as one sequence of 64-key
+//     tiles.  Three LDS buffers hold dequantized tiles: while the waves
+//     compute with tiles t and t+1, the workgroup dequantizes tile t+2 from
+//     packed codes it loaded one tile earlier and loads the codes of tile
+//     t+3.  Dequantization is exact: E2M1 x E4M3 has at most 6 significant
+//     bits and lies in [2^-10, 2688], so it fits f16; the hardware converts
+//     two FP4 codes to f16 (scale 1) and one packed f16 multiply applies the
+//     block scale;
 //   * each wave computes S^T = K Q^T so that a lane owns one query row in
 //     both the score and the output accumulators: the softmax row max and sum
 //     stay inside a lane plus one exchange with the lane 32 away;
 //   * O^T += V^T P^T, with P taken straight from the score registers and V
-//     read dimension-major, as the cache stores it.
+//     read dimension-major, as the cache stores it;
+//   * software pipeline with one barrier per tile: the MFMAs of S(t+1) are
+//     issued together with the exp2 work of tile t, and the MFMAs of V(t) P(t)
+//     together with the dequantization of tile t+2, the loads of tile t+3
+//     and the mask and row max of S(t+1), so that the matrix core and the
+//     vector ALU of a SIMD are busy at the same time.
 //
 // Rotation: the cache holds keys before rotation.  Rotating q by pos(qf) and
 // k by pos(kf) gives the same score as rotating q by pos(qf) - pos(kf), so
 // each wave turns its rotated queries back by -pos(kf) once per key frame and
-// the keys need no rotation.
+// the keys need no rotation.  The cos/sin rows of these turns are staged in
+// LDS once per workgroup.
 //
 // Precision: the turned-back queries are split into an f16 high part and an
 // f16 low part (two MFMAs on the same exact key operand), so scores carry
@@ -42,12 +50,22 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128;   // query rows per workgroup
-constexpr int kBN = 64;    // keys per tile
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;               // two groups of 4, one wave of each per SIMD
 constexpr int kThreads = kWaves * 64;
-constexpr int kPad = 8;    // f16 elements of padding per LDS row
-constexpr int kXcds = 8;   // accelerator complex dies of MI355X
+constexpr int kBM = kWaves * 32;        // query rows per workgroup
+constexpr int kBN = 64;                 // keys per tile
+constexpr int kPad = 8;                 // f16 elements of padding per LDS row
+constexpr int kXcds = 8;                // accelerator complex dies of MI355X
+constexpr int kKBufs = 2, kVBufs = 3;   // dequantized K and V tiles in LDS
+
+// Buffer resource (gfx9 format) over `bytes` bytes at `base`: loads at
+// offsets past the end return zero instead of touching memory.
+constexpr uint32_t kBufferWord3 = 0x00020000u;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, (int)bytes,
+                                           (int)kBufferWord3);
+}
 
 __device__ __forceinline__ f16x8 as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ uint32_t bits(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
@@ -90,10 +108,16 @@ __device__ __forceinline__ int sigma(int m) {
   return 16 * (i >> 1) + 8 * hh + 4 * (i & 1) + r;
 }
 
+// Physical LDS row of key k in a K tile: rows 8..15 of every 16 swap their
+// halves, so the 8 lanes that read together (keys {0-3, 8-11} + 16j and
+// {4-7, 12-15} + 16j under sigma) hit 8 different bank groups.
+__device__ __forceinline__ int krow_phys(int k) { return k ^ (((k >> 3) & 1) << 2); }
+
 template <int D>
 struct Smem {
-  uint16_t kh[2][kBN][D + kPad];   // dequantized K tiles, f16 bits
-  uint16_t vt[2][D][kBN + kPad];   // dequantized V tiles, dimension-major
+  uint16_t kh[kKBufs][kBN][D + kPad];   // dequantized K tiles, f16 bits
+  uint16_t vt[kVBufs][D][kBN + kPad];   // dequantized V tiles, dimension-major
+  float2 rot[FP4KV_MAX_SLOTS][D / 2];  // (cos, sin) of the turn into each listed frame
   int fl_slot[FP4KV_MAX_SLOTS];
   int fl_kf[FP4KV_MAX_SLOTS];
   int fl_pos[FP4KV_MAX_SLOTS];
@@ -103,59 +127,82 @@ struct Smem {
   int n_fl;
 };
 
-// Packed codes and scales of one tile held by one thread between the load
-// and the dequantization.
-struct Raw {
-  uint4 kc;        // 32 key elements (16 bytes) of one key
+// Packed codes and scales held by one thread between the load and the
+// dequantization: one key's 32 elements, or 16 tokens of two value dimensions.
+struct RawK {
+  uint4 kc;        // 32 key elements (16 bytes)
   uint32_t ks;     // their two block scales (low 16 bits)
+};
+struct RawV {
   uint2 vc[2];     // 16 tokens of two value dimensions
   uint4 vs;        // the 16 tokens' scales of that value block
 };
 
-// Loads are unconditional (addresses clamped into the frame, results
-// zeroed afterwards) so the compiler keeps them in flight across the compute
-// of the current tile instead of waiting at a branch.
+// Buffer loads over the (head, slot) ranges of the cache: keys past Tc fall
+// outside the K range and read as zero, value tokens past Tv are sent out of
+// range.  No branch, so the loads stay in flight until the codes are
+// dequantized two phases later.  lt is the thread's index in its group.
+template <bool K>
+struct RawOf {
+  using type = RawV;
+};
+template <>
+struct RawOf<true> {
+  using type = RawK;
+};
+
+// Buffer resources over one (head, slot) range of the four cache arrays.
+struct SlotRes {
+  __amdgpu_buffer_rsrc_t kc, ks, vc, vs;
+};
 template <int D>
-__device__ __forceinline__ void load_tile(const AttnParams &p, int head, int slot, int k0,
-                                          int nval, Raw &r) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ SlotRes slot_resources(const AttnParams &p, int head, int slot) {
+  const long long hs = (long long)head * p.n_slots + slot;
+  SlotRes r;
+  r.kc = rsrc(p.k_codes + hs * p.Tc * (D / 2), p.Tc * (D / 2));
+  r.ks = rsrc(p.k_scales + hs * p.Tc * (D / 16), p.Tc * (D / 16));
+  r.vc = rsrc(p.v_codes + hs * D * (p.Tv / 2), D * (p.Tv / 2));
+  r.vs = rsrc(p.v_scales + hs * (D / 16) * p.Tv, (D / 16) * p.Tv);
+  return r;
+}
+
+template <int D>
+__device__ __forceinline__ void load_k(const SlotRes &sr, int k0, int lt, RawK &r) {
   constexpr int KU = D / 32;
-  if (tid < kBN * KU) {   // all threads for D = 128
-    const int key = tid / KU, qd = tid % KU;
-    const bool ok = key < nval;
-    const long long row = ((long long)head * p.n_slots + slot) * p.Tc + k0 + (ok ? key : 0);
-    const uint4 kc = *(const uint4 *)(p.k_codes + row * (D / 2) + 16 * qd);
-    const uint32_t ks = *(const uint16_t *)(p.k_scales + row * (D / 16) + 2 * qd);
-    r.kc = ok ? kc : make_uint4(0, 0, 0, 0);
-    r.ks = ok ? ks : 0u;
+  if (lt < kBN * KU) {   // every thread of the group for D = 128
+    const uint32_t key = k0 + lt / KU, qd = lt % KU;
+    const auto kc = __builtin_amdgcn_raw_buffer_load_b128(sr.kc, key * (D / 2) + 16 * qd, 0, 0);
+    r.kc = make_uint4(kc[0], kc[1], kc[2], kc[3]);
+    r.ks = __builtin_amdgcn_raw_buffer_load_b16(sr.ks, key * (D / 16) + 2 * qd, 0, 0);
   }
-  if (tid < 2 * D) {
-    const int rp = tid >> 2, kg = tid & 3;
+}
+template <int D>
+__device__ __forceinline__ void load_v(const SlotRes &sr, int Tv, int k0, int lt, RawV &r) {
+  if (lt < 2 * D) {
+    const int rp = lt >> 2, kg = lt & 3;
     const int tok = k0 + 16 * kg;
-    const bool ok = tok < p.Tv;
-    const int tk = ok ? tok : 0;
-    const long long drow = ((long long)head * p.n_slots + slot) * D + 2 * rp;
-    const uint2 c0 = *(const uint2 *)(p.v_codes + drow * (p.Tv / 2) + tk / 2);
-    const uint2 c1 = *(const uint2 *)(p.v_codes + (drow + 1) * (p.Tv / 2) + tk / 2);
-    const long long srow = ((long long)head * p.n_slots + slot) * (D / 16) + (2 * rp) / 16;
-    const uint4 vs = *(const uint4 *)(p.v_scales + srow * p.Tv + tk);
-    r.vc[0] = ok ? c0 : make_uint2(0, 0);
-    r.vc[1] = ok ? c1 : make_uint2(0, 0);
-    r.vs = ok ? vs : make_uint4(0, 0, 0, 0);
+    const bool ok = tok < Tv;
+    const uint32_t o0 = ok ? (uint32_t)(2 * rp * (Tv / 2) + tok / 2) : kOutOfRange;
+    const uint32_t o1 = ok ? o0 + (uint32_t)(Tv / 2) : kOutOfRange;
+    const uint32_t os = ok ? (uint32_t)((2 * rp / 16) * Tv + tok) : kOutOfRange;
+    const auto c0 = __builtin_amdgcn_raw_buffer_load_b64(sr.vc, o0, 0, 0);
+    const auto c1 = __builtin_amdgcn_raw_buffer_load_b64(sr.vc, o1, 0, 0);
+    const auto vs = __builtin_amdgcn_raw_buffer_load_b128(sr.vs, os, 0, 0);
+    r.vc[0] = make_uint2(c0[0], c0[1]);
+    r.vc[1] = make_uint2(c1[0], c1[1]);
+    r.vs = make_uint4(vs[0], vs[1], vs[2], vs[3]);
   }
 }
 
-// Physical LDS row of key k in a K tile: rows 8..15 of every 16 swap their
-// halves, so the 8 lanes that read together (keys {0-3, 8-11} + 16j and
-// {4-7, 12-15} + 16j under sigma) hit 8 different bank groups.
-__device__ __forceinline__ int krow_phys(int k) { return k ^ (((k >> 3) & 1) << 2); }
-
+// K rows past the end of the frame read as zero codes (their scores are
+// masked).  V tokens past the end of the frame are the cache's zero padding
+// (codes and scales are written as zeros up to Tv) or read as zero, so they
+// decode to zero and add nothing to V P.
 template <int D>
-__device__ __forceinline__ void dequant_tile(const Raw &r, int nval, Smem<D> &sm, int buf) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void dequant_k(const RawK &r, int lt, uint16_t (*kt)[D + kPad]) {
   constexpr int KU = D / 32;
-  if (tid < kBN * KU) {
-    const int key = tid / KU, qd = tid % KU;
+  if (lt < kBN * KU) {
+    const int key = lt / KU, qd = lt % KU;
     const f16x2 s2 = fp8x2<false>(r.ks);
     const f16x2 sa = {s2[0], s2[0]}, sb = {s2[1], s2[1]};
     const uint32_t cw[4] = {r.kc.x, r.kc.y, r.kc.z, r.kc.w};
@@ -168,14 +215,15 @@ __device__ __forceinline__ void dequant_tile(const Raw &r, int nval, Smem<D> &sm
       o[4 * w + 2] = bits(fp4x2<2>(cw[w]) * sc);
       o[4 * w + 3] = bits(fp4x2<3>(cw[w]) * sc);
     }
-    // rows past the end of the frame were not loaded: they hold zeros, and
-    // zero codes decode to zero
-    uint4 *dst = (uint4 *)&sm.kh[buf][krow_phys(key)][32 * qd];
+    uint4 *dst = (uint4 *)&kt[krow_phys(key)][32 * qd];
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
   }
-  if (tid < 2 * D) {
-    const int rp = tid >> 2, kg = tid & 3;
+}
+template <int D>
+__device__ __forceinline__ void dequant_v(const RawV &r, int lt, uint16_t (*vt)[kBN + kPad]) {
+  if (lt < 2 * D) {
+    const int rp = lt >> 2, kg = lt & 3;
     const uint32_t sw[4] = {r.vs.x, r.vs.y, r.vs.z, r.vs.w};
     f16x2 sc[8];   // scales of token pairs (2j, 2j+1)
 #pragma unroll
@@ -183,7 +231,6 @@ __device__ __forceinline__ void dequant_tile(const Raw &r, int nval, Smem<D> &sm
       sc[2 * w] = fp8x2<false>(sw[w]);
       sc[2 * w + 1] = fp8x2<true>(sw[w]);
     }
-    const int valid = nval - 16 * kg;   // tokens of this unit inside the frame
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const uint32_t cw[2] = {r.vc[rr].x, r.vc[rr].y};
@@ -195,18 +242,125 @@ __device__ __forceinline__ void dequant_tile(const Raw &r, int nval, Smem<D> &sm
         o[4 * w + 2] = bits(fp4x2<2>(cw[w]) * sc[4 * w + 2]);
         o[4 * w + 3] = bits(fp4x2<3>(cw[w]) * sc[4 * w + 3]);
       }
-      if (valid < 16) {   // tail of the frame: padding tokens contribute zero
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t keep = (2 * j + 1 < valid) ? 0xFFFFFFFFu : (2 * j < valid ? 0xFFFFu : 0u);
-          o[j] &= keep;
-        }
-      }
-      uint4 *dst = (uint4 *)&sm.vt[buf][2 * rp + rr][16 * kg];
+      uint4 *dst = (uint4 *)&vt[2 * rp + rr][16 * kg];
       dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
       dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
     }
   }
+}
+
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100, kSgDsWrite = 0x200;
+
+// S^T (64 keys x the wave's 32 query rows) = K (Q_hi + Q_lo)^T.  The K
+// operands are read two k-steps ahead of their MFMAs.
+template <int D>
+__device__ __forceinline__ void scores(f32x16 (&s)[2], const uint16_t (*kt)[D + kPad], int krow,
+                                       int hf, const f16x8 (&qhi)[D / 16],
+                                       const f16x8 (&qlo)[D / 16]) {
+  constexpr int KS = D / 16;
+  f16x8 ka[2][2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s[b][j] = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      ka[kk][b] = as_f16x8(*(const uint4 *)&kt[32 * b + krow][16 * kk + 8 * hf]);
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const f16x8 k0 = ka[kk & 1][0], k1 = ka[kk & 1][1];
+    s[0] = mfma32(k0, qhi[kk], s[0]);
+    s[1] = mfma32(k1, qhi[kk], s[1]);
+    s[0] = mfma32(k0, qlo[kk], s[0]);
+    s[1] = mfma32(k1, qlo[kk], s[1]);
+    if (kk + 2 < KS) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        ka[kk & 1][b] = as_f16x8(*(const uint4 *)&kt[32 * b + krow][16 * (kk + 2) + 8 * hf]);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
+    if (kk + 2 < KS) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
+    if (kk + 2 < KS) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+  }
+}
+
+// P = exp2(s * cf - m) rounded to f16 as four P^T operands of 16 keys, and
+// l += sum of P.
+__device__ __forceinline__ void softmax_weights(const f32x16 (&s)[2], float cf, float m,
+                                                float &l, f16x8 (&pb)[4]) {
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  float lb[2] = {0.0f, 0.0f};   // two independent sums
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b][8 * t2 + 2 * e], cf, -m));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b][8 * t2 + 2 * e + 1], cf, -m));
+        const f16x2 ph = {(_Float16)p0, (_Float16)p1};
+        lb[b] = __builtin_amdgcn_fdot2(ph, ones, lb[b], false);
+        w[e] = bits(ph);
+      }
+      pb[2 * b + t2] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
+    }
+  l += lb[0] + lb[1];
+}
+
+// O^T += V^T P^T over the four slices of 16 keys of a tile.  The V operands
+// of a slice are read while the MFMAs of the previous slice issue.
+template <int D>
+__device__ __forceinline__ void accumulate_pv(f32x16 (&o)[D / 32], const uint16_t (*vt)[kBN + kPad],
+                                              int n, int hf, const f16x8 (&pb)[4]) {
+  constexpr int DB = D / 32;
+  f16x8 va[2][DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) va[0][db] = as_f16x8(*(const uint4 *)&vt[32 * db + n][8 * hf]);
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, DB, 0);
+#pragma unroll
+  for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      if (t4 + 1 < 4)
+        va[(t4 + 1) & 1][db] =
+            as_f16x8(*(const uint4 *)&vt[32 * db + n][16 * (t4 + 1) + 8 * hf]);
+      o[db] = mfma32(va[t4 & 1][db], pb[t4], o[db]);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      if (t4 + 1 < 4) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgValu, 3, 0);
+      if (t4 == 1) __builtin_amdgcn_sched_group_barrier(kSgDsWrite, 1, 0);
+    }
+}
+
+// Masks the scores of keys at or past nval and of rows that do not see the
+// frame, and returns the row maximum times cf (-inf for a fully masked row).
+template <bool MASK>
+__device__ __forceinline__ float mask_and_max(f32x16 (&s)[2], bool vis, int nval, int hf,
+                                              float cf) {
+  if (MASK) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = 32 * b + 16 * (j >> 3) + 8 * hf + (j & 7);
+        s[b][j] = (vis && key < nval) ? s[b][j] : -INFINITY;
+      }
+  }
+  float part[4];   // four independent chains of 8
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    part[c] = s[c >> 1][8 * (c & 1)];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) part[c] = fmaxf(part[c], s[c >> 1][8 * (c & 1) + j]);
+  }
+  const float tmax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+  return halves_max(tmax) * cf;
 }
 
 template <int D>
@@ -218,8 +372,41 @@ __host__ __device__ constexpr size_t smem_bytes() { return sizeof(Smem<D>); }
 // rarely.
 constexpr float kTau = 8.0f;
 
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
+// Position of a tile in the walk: listed frame fi, tile tt within the frame,
+// index i in the walk.
+struct Cursor {
+  int fi, tt, i;
+};
+
+// Workgroup barrier that orders LDS accesses only, so the global loads
+// issued before it stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Ping-pong schedule.  The 8 waves form two groups of 4 with one wave of
+// each group on every SIMD; both groups walk the same tiles for different
+// query rows, offset by one phase.  Phases end at workgroup barriers, and in
+// every phase one group issues MFMAs while the other does the softmax:
+//   MFMA phase of step t:  O += V(t-1) P(t-1), S(t) = K(t) Q'^T, and in the
+//                          shadow of these MFMAs one half of a later tile
+//                          dequantized (group 0: V of tile t+1, group 1: K of
+//                          tile t+1) and the codes of its next half loaded;
+//   VALU phase of step t:  mask, row max and rescale of S(t), P(t) and l; the
+//                          queries turned into the frame of tile t+1.
+// Group 0 runs MFMA phases on even phases 2t, group 1 on odd phases 2t+1
+// after an empty opening phase.  K(t) is written in phase 2t-1 and read in
+// phases 2t and 2t+1 (2 buffers); V(t) is written in phase 2t-2 and read in
+// phases 2t+2 and 2t+3 (3 buffers).
 template <int D, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
   constexpr int KS = D / 16;   // k-steps of S^T over d
   constexpr int DB = D / 32;   // 32-row blocks of O^T
   extern __shared__ __align__(16) uint8_t smem_raw[];
@@ -228,6 +415,8 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, hf = lane >> 5;
+  const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);
+  const int lt = tid & 255;   // thread index within the group
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
   // L2).  Give XCD x the contiguous work items [x*per, (x+1)*per) in
   // head-major order, so each head's FP4 KV is read into few L2s.
@@ -281,57 +470,42 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
   const int n_fl = sm.n_fl;
   const int n_tiles = (p.Tc + kBN - 1) / kBN;
   const int last_nval = p.Tc - (n_tiles - 1) * kBN;
+  const int half_rot = p.rot_dim >> 1;
+
+  // ---- turn into listed frame fi: R(-(pos(fi) - pos(fi - 1))), pos(-1) = 0;
+  // pairs past rot_dim / 2 get the identity (1, 0)
+  for (int i = tid; i < n_fl * (D / 2); i += kThreads) {
+    const int fi = i / (D / 2), j = i % (D / 2);
+    const int dpos = sm.fl_pos[fi] - (fi > 0 ? sm.fl_pos[fi - 1] : 0);
+    float2 cs = make_float2(1.0f, 0.0f);
+    if (j < half_rot) {
+      const float2 t = *(const float2 *)(p.cos_sin + (long long)abs(dpos) * p.rot_dim + 2 * j);
+      cs = make_float2(t.x, dpos >= 0 ? -t.y : t.y);
+    }
+    sm.rot[fi][j] = cs;
+  }
 
   f32x16 oacc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b)
 #pragma unroll
     for (int j = 0; j < 16; ++j) oacc[b][j] = 0.0f;
-  float m_run = -1.0e30f, l_part = 0.0f, gv_cur = 1.0f;
-  const int half_rot = p.rot_dim >> 1;
-  const int krow = krow_phys(sigma(n));   // + 32 b for key block b
-  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-  const long long qoff = ((long long)(row_ok ? my_row : 0) * p.H + head) * D + 8 * hf;
-  f16x8 qhi[KS], qlo[KS];
-  int prev_pos = 0;
+  float m_run = -1.0e30f, l_part = 0.0f, gv_last = 1.0f;
 
-  Raw raw;
-  int buf = 0;
   if (n_fl > 0) {
-    const int nv0 = n_tiles == 1 ? last_nval : kBN;
-    load_tile<D>(p, head, sm.fl_slot[0], 0, nv0, raw);
-    dequant_tile<D>(raw, nv0, sm, 0);
-  }
-  __syncthreads();
+    const int krow = krow_phys(sigma(n));   // + 32 b for key block b
+    const long long qoff = ((long long)(row_ok ? my_row : 0) * p.H + head) * D + 8 * hf;
+    const int n_total = n_fl * n_tiles;
+    f16x8 qhi[KS], qlo[KS];
 
-  for (int fi = 0; fi < n_fl; ++fi) {
-    // ---- new key frame: visibility, tensor scales, turned-back queries
-    const int kf = sm.fl_kf[fi], pos = sm.fl_pos[fi];
-    const float gv = sm.fl_gv[fi];
-    const bool lane_vis =
-        row_ok && (kf / p.C <= my_qchunk) && (kf < p.S || sm.fl_shot[fi] == my_qshot);
-    const bool wave_any = __ballot(lane_vis) != 0ull;
-    const bool wave_all = __ballot(lane_vis) == ~0ull;
-    if (fi > 0) {   // keep O = g_v * acc across the change of tensor scale
-      const float ratio = __fdiv_rn(gv_cur, gv);
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[b][j] *= ratio;
-    }
-    gv_cur = gv;
-    const float cf = p.scale_log2 * sm.fl_gk[fi];
-    // Queries turned back by -pos(kf) as f16 hi + lo.  The first frame reads
-    // the rotated queries; later frames turn the previous frame's queries by
-    // -(pos(kf) - pos(prev)), so the queries are read from memory once.
-    {
-      const int dpos = fi == 0 ? pos : pos - prev_pos;
-      const float sgn = dpos >= 0 ? -1.0f : 1.0f;   // R(-dpos) = (c, -s) of |dpos|
-      const float *tab = p.cos_sin + (long long)abs(dpos) * p.rot_dim;
+    // Turns the queries into listed frame fi: the first frame reads the
+    // rotated queries from memory, later frames turn the previous frame's.
+    auto turn_queries = [&](int fi, bool from_memory) __attribute__((always_inline)) {
+      const float2 *rot = sm.rot[fi];
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         float x[8];
-        if (fi == 0) {
+        if (from_memory) {
           if (p.q_f32) {
             const float4 a = *(const float4 *)((const float *)p.q + qoff + 16 * kk);
             const float4 b = *(const float4 *)((const float *)p.q + qoff + 16 * kk + 4);
@@ -355,12 +529,9 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int pair = 8 * kk + 4 * hf + e;
-          float ra = x[2 * e], rb = x[2 * e + 1];
-          if (pair < half_rot) {
-            const float2 cs = *(const float2 *)(tab + 2 * pair);
-            rotate_pair(x[2 * e], x[2 * e + 1], cs.x, sgn * cs.y, ra, rb);
-          }
+          const float2 cs = rot[8 * kk + 4 * hf + e];
+          float ra, rb;
+          rotate_pair(x[2 * e], x[2 * e + 1], cs.x, cs.y, ra, rb);
           const f16x2 h2 = {(_Float16)ra, (_Float16)rb};
           const f16x2 l2 = {(_Float16)(ra - (float)h2[0]), (_Float16)(rb - (float)h2[1])};
           hw[e] = bits(h2);
@@ -369,124 +540,150 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnParams p) {
         qhi[kk] = as_f16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
         qlo[kk] = as_f16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
-    }
-    prev_pos = pos;
+    };
 
-    for (int t = 0; t < n_tiles; ++t) {
-      const int nval = t == n_tiles - 1 ? last_nval : kBN;
-      // ---- prefetch the next tile's packed codes and scales
-      const bool has_next = t + 1 < n_tiles || fi + 1 < n_fl;
-      int nval_next = 0;
-      if (has_next) {
-        const bool same = t + 1 < n_tiles;
-        const int tn = same ? t + 1 : 0;
-        nval_next = tn == n_tiles - 1 ? last_nval : kBN;
-        load_tile<D>(p, head, sm.fl_slot[same ? fi : fi + 1], tn * kBN, nval_next, raw);
+    // Next tile of the walk (the last tile stays put).
+    auto advance = [&](Cursor c) __attribute__((always_inline)) {
+      if (c.fi == n_fl - 1 && c.tt == n_tiles - 1) return c;
+      ++c.i;
+      if (++c.tt == n_tiles) {
+        c.tt = 0;
+        ++c.fi;
       }
+      return c;
+    };
+    // Per-frame values of the frame of the tile whose softmax comes next:
+    // visibility of this lane's row, whether the whole wave sees the frame,
+    // the exp2 factor softmax_scale * log2(e) * g_k and the value scale g_v.
+    // f_ratio = g_v(previous frame) / g_v(this frame) keeps O = g_v * acc.
+    bool f_vis = false, f_all = false;
+    float f_cf = 0.0f, f_gv = 1.0f, f_ratio = 1.0f;
+    auto load_frame = [&](int fi) __attribute__((always_inline)) {
+      const int kf = sm.fl_kf[fi];
+      f_vis = row_ok & (kf / p.C <= my_qchunk) & ((kf < p.S) | (sm.fl_shot[fi] == my_qshot));
+      f_all = __ballot(f_vis) == ~0ull;
+      f_cf = p.scale_log2 * sm.fl_gk[fi];
+      const float gv = sm.fl_gv[fi];
+      f_ratio = __fdiv_rn(f_gv, gv);
+      f_gv = gv;
+    };
 
-      if (wave_any) {
-        // ---- S^T = K (Q_hi + Q_lo)^T for 2 blocks of 32 keys
-        // all 16 K operands are read first; the MFMAs then alternate between
-        // the two key blocks so consecutive MFMAs never share an accumulator
-        f32x16 sacc[2];
-        f16x8 ka[2][KS];
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk)
-            ka[b][kk] = as_f16x8(*(const uint4 *)&sm.kh[buf][32 * b + krow][16 * kk + 8 * hf]);
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) sacc[b][j] = 0.0f;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          sacc[0] = mfma32(ka[0][kk], qhi[kk], sacc[0]);
-          sacc[1] = mfma32(ka[1][kk], qhi[kk], sacc[1]);
-          sacc[0] = mfma32(ka[0][kk], qlo[kk], sacc[0]);
-          sacc[1] = mfma32(ka[1][kk], qlo[kk], sacc[1]);
-        }
-        __builtin_amdgcn_s_setprio(0);
-        // ---- mask (tail tiles and rows that do not see this frame)
-        if (!(wave_all && nval == kBN)) {
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const int key = 32 * b + 16 * (j >> 3) + 8 * hf + (j & 7);
-              sacc[b][j] = (lane_vis && key < nval) ? sacc[b][j] : -INFINITY;
-            }
-        }
-        // ---- online softmax, exp2 argument = s * cf - m
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, sacc[b][j]);
-        tmax = halves_max(tmax) * cf;
-        const bool grow = tmax > m_run + kTau;
-        if (__ballot(grow) != 0ull) {
+    // Each group dequantizes one half (group 0: V, group 1: K) of the tiles
+    // in walk order; cd is the next tile whose codes are loaded or loading.
+    // The two groups run the same walk; group 1 dequantizes K halves and
+    // group 0 V halves, so each group's code holds only its own codes.
+    auto run_group = [&](auto gtag) __attribute__((always_inline)) {
+      constexpr bool G = decltype(gtag)::value;
+      typename RawOf<G>::type raw;
+      Cursor cd = {0, 0, 0};
+      SlotRes res = slot_resources<D>(p, head, sm.fl_slot[0]);   // frame of cd
+      auto load_half = [&]() __attribute__((always_inline)) {
+        if constexpr (G) load_k<D>(res, cd.tt * kBN, lt, raw);
+        else load_v<D>(res, p.Tv, cd.tt * kBN, lt, raw);
+      };
+      // Dequantizes the half tile cd.i into its buffer and loads the codes of
+      // the next one.  Past the end of the walk the loads repeat the last
+      // tile and the dequantized copies land in buffers no phase reads.
+      auto dequant_next = [&]() __attribute__((always_inline)) {
+        if constexpr (G) dequant_k<D>(raw, lt, sm.kh[cd.i % kKBufs]);
+        else dequant_v<D>(raw, lt, sm.vt[cd.i % kVBufs]);
+        Cursor nx = advance(cd);
+        nx.i = cd.i + 1;
+        if (nx.fi != cd.fi) res = slot_resources<D>(p, head, sm.fl_slot[nx.fi]);
+        cd = nx;
+        load_half();
+      };
+
+      // ---- prologue: tile 0 dequantized, the codes of tile 1 loading
+      load_half();
+      dequant_next();
+      lds_barrier();   // tile 0, the turn table and the frame list are in LDS
+
+      turn_queries(0, true);
+      load_frame(0);
+      Cursor ct = {0, 0, 0};   // tile of this group's next S and softmax
+      f32x16 s[2];
+      f16x8 pb[4];
+
+      // Softmax of tile t (ct): mask, row max, lazy rescale of O and l
+      // together with the g_v ratio on the first tile of a frame, then P and l.
+      auto softmax_tile = [&](auto masked) __attribute__((always_inline)) {
+        const int nval = ct.tt == n_tiles - 1 ? last_nval : kBN;
+        const float tmax = mask_and_max<decltype(masked)::value>(s, f_vis, nval, hf, f_cf);
+        const bool first = ct.i > 0 && ct.tt == 0;
+        float factor = first ? f_ratio : 1.0f;
+        bool scale_o = first;
+        if (__ballot(tmax > m_run + kTau) != 0ull) {
           const float m_new = fmaxf(m_run, tmax);
           const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
           m_run = m_new;
           l_part *= alpha;
-#pragma unroll
+          factor *= alpha;
+          scale_o = true;
+        }
+        if (scale_o) {
+  #pragma unroll
           for (int b = 0; b < DB; ++b)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) oacc[b][j] *= alpha;
+  #pragma unroll
+            for (int j = 0; j < 16; ++j) oacc[b][j] *= factor;
         }
-        f16x8 pb[4];
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2) {
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[b][8 * t2 + 2 * e], cf, -m_run));
-              const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[b][8 * t2 + 2 * e + 1], cf, -m_run));
-              const f16x2 ph = {(_Float16)p0, (_Float16)p1};
-              l_part = __builtin_amdgcn_fdot2(ph, ones, l_part, false);
-              w[e] = bits(ph);
-            }
-            pb[2 * b + t2] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
-          }
-        // ---- O^T += V^T P^T, 4 slices of 16 keys
-        // V operands are read DB ahead of their MFMA
-        __builtin_amdgcn_s_setprio(1);
-        f16x8 va[4][DB];
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          va[0][db] = as_f16x8(*(const uint4 *)&sm.vt[buf][32 * db + n][8 * hf]);
-        __builtin_amdgcn_sched_group_barrier(0x100, DB, 0);
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            if (t4 + 1 < 4)
-              va[t4 + 1][db] =
-                  as_f16x8(*(const uint4 *)&sm.vt[buf][32 * db + n][16 * (t4 + 1) + 8 * hf]);
-            oacc[db] = mfma32(va[t4][db], pb[t4], oacc[db]);
-            if (t4 + 1 < 4) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            } else {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            }
-          }
-        }
-        __builtin_amdgcn_s_setprio(0);
-      }
+        softmax_weights(s, f_cf, m_run, l_part, pb);
+      };
 
-      if (has_next) dequant_tile<D>(raw, nval_next, sm, buf ^ 1);
-      buf ^= 1;
-      __syncthreads();
-    }
+      // VALU phase of step t: softmax of tile t, then the queries turned into
+      // the frame of tile t+1
+      auto valu_phase = [&](int t) __attribute__((always_inline)) {
+        if (t < n_total) {
+          if (!f_all || (ct.tt == n_tiles - 1 && last_nval < kBN))
+            softmax_tile(BoolC<true>());
+          else
+            softmax_tile(BoolC<false>());
+        }
+        if (t + 1 < n_total) {
+          const Cursor cn = advance(ct);
+          if (cn.fi != ct.fi) {
+            turn_queries(cn.fi, false);
+            load_frame(cn.fi);
+          }
+          ct = cn;
+        }
+      };
+
+      // MFMA phase of step t, with the dequantization of the group's next
+      // half tile in the shadow of the MFMAs.  P is consumed first and S
+      // produced last, which keeps the registers of P, the dequantization and
+      // S from being live at the same time.
+      auto mfma_phase = [&](int t, auto has_pv, auto has_s) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
+        if constexpr (decltype(has_pv)::value)
+          accumulate_pv<D>(oacc, sm.vt[(t + kVBufs - 1) % kVBufs], n, hf, pb);
+        dequant_next();
+        if constexpr (decltype(has_s)::value)
+          scores<D>(s, sm.kh[t % kKBufs], krow, hf, qhi, qlo);
+        __builtin_amdgcn_s_setprio(0);
+        lds_barrier();
+      };
+
+      if (G) lds_barrier();   // group 1's opening phase
+      mfma_phase(0, BoolC<false>(), BoolC<true>());
+      valu_phase(0);
+      lds_barrier();
+      for (int t = 1; t < n_total; ++t) {
+        mfma_phase(t, BoolC<true>(), BoolC<true>());
+        valu_phase(t);
+        lds_barrier();
+      }
+      mfma_phase(n_total, BoolC<true>(), BoolC<false>());
+      if (!G) lds_barrier();   // group 0's closing phase
+      gv_last = f_gv;
+    };
+    if (grp) run_group(BoolC<true>());
+    else run_group(BoolC<false>());
   }
 
-  // ---- epilogue: O = g_v * acc / l
+  // ---- epilogue: O = g_v * acc / l, g_v of the last frame walked
   const float l = halves_sum(l_part);
-  const float inv = l > 0.0f ? __fdiv_rn(gv_cur, l) : 0.0f;
+  const float inv = l > 0.0f ? __fdiv_rn(gv_last, l) : 0.0f;
   if (!row_ok) return;
   const long long obase = ((long long)my_row * p.H + head) * D;
 #pragma unroll
