@@ -313,26 +313,31 @@ __device__ __forceinline__ void softmax_weights(const f32x16 (&s)[2], float cf, 
   l += lb[0] + lb[1];
 }
 
-// O^T += V^T P^T over the four slices of 16 keys of a tile.  The V operands
-// of a slice are read while the MFMAs of the previous slice issue.
+// V^T operands of a tile for this wave: slice t4 (16 keys), block db (32
+// dimensions) in va[t4 * (D / 32) + db].  They are read in the softmax phase
+// before the MFMA phase that uses them.
 template <int D>
-__device__ __forceinline__ void accumulate_pv(f32x16 (&o)[D / 32], const uint16_t (*vt)[kBN + kPad],
-                                              int n, int hf, const f16x8 (&pb)[4]) {
+__device__ __forceinline__ void read_v_operands(f16x8 (&va)[D / 8],
+                                                const uint16_t (*vt)[kBN + kPad], int n, int hf) {
   constexpr int DB = D / 32;
-  f16x8 va[2][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) va[0][db] = as_f16x8(*(const uint4 *)&vt[32 * db + n][8 * hf]);
-  __builtin_amdgcn_sched_group_barrier(kSgDsRead, DB, 0);
+  for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      va[t4 * DB + db] = as_f16x8(*(const uint4 *)&vt[32 * db + n][16 * t4 + 8 * hf]);
+}
+
+// O^T += V^T P^T over the four slices of 16 keys of a tile.
+template <int D>
+__device__ __forceinline__ void accumulate_pv(f32x16 (&o)[D / 32], const f16x8 (&va)[D / 8],
+                                              const f16x8 (&pb)[4]) {
+  constexpr int DB = D / 32;
 #pragma unroll
   for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      if (t4 + 1 < 4)
-        va[(t4 + 1) & 1][db] =
-            as_f16x8(*(const uint4 *)&vt[32 * db + n][16 * (t4 + 1) + 8 * hf]);
-      o[db] = mfma32(va[t4 & 1][db], pb[t4], o[db]);
+      o[db] = mfma32(va[t4 * DB + db], pb[t4], o[db]);
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      if (t4 + 1 < 4) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSgValu, 3, 0);
       if (t4 == 1) __builtin_amdgcn_sched_group_barrier(kSgDsWrite, 1, 0);
     }
@@ -389,6 +394,14 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Workgroup barrier for a wave that has written nothing to LDS since the
+// last barrier: its own LDS reads may still be in flight (their data is not
+// overwritten until several phases later).  The memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_reads_in_flight() {
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // Ping-pong schedule.  The 8 waves form two groups of 4 with one wave of
@@ -604,6 +617,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
       Cursor ct = {0, 0, 0};   // tile of this group's next S and softmax
       f32x16 s[2];
       f16x8 pb[4];
+      f16x8 va[D / 8];   // V operands of the tile whose PV comes next
 
       // Softmax of tile t (ct): mask, row max, lazy rescale of O and l
       // together with the g_v ratio on the first tile of a frame, then P and l.
@@ -647,6 +661,9 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
           }
           ct = cn;
         }
+        // V operands of tile t for the next MFMA phase (V(t) has been in LDS
+        // since phase 2t-2 and is overwritten only in phase 2t+4)
+        read_v_operands<D>(va, sm.vt[t % kVBufs], n, hf);
       };
 
       // MFMA phase of step t, with the dequantization of the group's next
@@ -655,8 +672,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
       // S from being live at the same time.
       auto mfma_phase = [&](int t, auto has_pv, auto has_s) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(1);
-        if constexpr (decltype(has_pv)::value)
-          accumulate_pv<D>(oacc, sm.vt[(t + kVBufs - 1) % kVBufs], n, hf, pb);
+        if constexpr (decltype(has_pv)::value) accumulate_pv<D>(oacc, va, pb);
         dequant_next();
         if constexpr (decltype(has_s)::value)
           scores<D>(s, sm.kh[t % kKBufs], krow, hf, qhi, qlo);
@@ -667,11 +683,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
       if (G) lds_barrier();   // group 1's opening phase
       mfma_phase(0, BoolC<false>(), BoolC<true>());
       valu_phase(0);
-      lds_barrier();
+      barrier_reads_in_flight();
       for (int t = 1; t < n_total; ++t) {
         mfma_phase(t, BoolC<true>(), BoolC<true>());
         valu_phase(t);
-        lds_barrier();
+        barrier_reads_in_flight();
       }
       mfma_phase(n_total, BoolC<true>(), BoolC<false>());
       if (!G) lds_barrier();   // group 0's closing phase
