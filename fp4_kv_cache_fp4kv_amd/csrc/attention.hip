@@ -346,19 +346,19 @@ __device__ __forceinline__ void accumulate_pv(f32x16 (&o)[D / 32], const f16x8 (
 }
 
 // Masks the scores of keys at or past nval and of rows that do not see the
-// frame.
-__device__ __forceinline__ void apply_mask(f32x16 (&s)[2], bool vis, int nval, int hf) {
+// frame, and returns the row maximum times cf (-inf for a fully masked row).
+template <bool MASK>
+__device__ __forceinline__ float mask_and_max(f32x16 (&s)[2], bool vis, int nval, int hf,
+                                              float cf) {
+  if (MASK) {
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int key = 32 * b + 16 * (j >> 3) + 8 * hf + (j & 7);
-      s[b][j] = (vis && key < nval) ? s[b][j] : -INFINITY;
-    }
-}
-
-// Row maximum of the (masked) scores times cf (-inf for a fully masked row).
-__device__ __forceinline__ float row_max(const f32x16 (&s)[2], float cf) {
+      for (int j = 0; j < 16; ++j) {
+        const int key = 32 * b + 16 * (j >> 3) + 8 * hf + (j & 7);
+        s[b][j] = (vis && key < nval) ? s[b][j] : -INFINITY;
+      }
+  }
   float part[4];   // four independent chains of 8
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -374,9 +374,8 @@ template <int D>
 __host__ __device__ constexpr size_t smem_bytes() { return sizeof(Smem<D>); }
 
 // Softmax rescaling is lazy: the reference maximum of a row moves only when
-// a weight reaches 2^15 against it, and then to the row maximum if that is
-// more than 2^kTau (log2 units) above the reference, so weights stay below
-// 2^15 (representable in f16) and the output accumulators are rescaled
+// a score exceeds it by more than 2^kTau (log2 units), so weights stay below
+// 2^kTau (representable in f16) and the output accumulators are rescaled
 // rarely.
 constexpr float kTau = 8.0f;
 
@@ -624,38 +623,27 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
 
       // Softmax of tile t (ct): mask, row max, lazy rescale of O and l
       // together with the g_v ratio on the first tile of a frame, then P and l.
-      // Softmax of tile t (ct).  The weights are first taken against the
-      // current reference maximum.  Only when one of them reaches 2^15
-      // (or the row has no reference yet, which gives inf) does the wave take
-      // the row maxima, raise the reference of the rows whose maximum passed
-      // it by more than 2^kTau, rescale O and l, and recompute the weights.
-      // The g_v ratio of a new frame is applied to O with the same pass.
       auto softmax_tile = [&](auto masked) __attribute__((always_inline)) {
-        if constexpr (decltype(masked)::value)
-          apply_mask(s, f_vis, ct.tt == n_tiles - 1 ? last_nval : kBN, hf);
+        const int nval = ct.tt == n_tiles - 1 ? last_nval : kBN;
+        const float tmax = mask_and_max<decltype(masked)::value>(s, f_vis, nval, hf, f_cf);
         const bool first = ct.i > 0 && ct.tt == 0;
         float factor = first ? f_ratio : 1.0f;
         bool scale_o = first;
-        float lt = 0.0f;
-        softmax_weights(s, f_cf, m_run, lt, pb);
-        if (__ballot(!(lt < 32768.0f)) != 0ull) {
-          const float tmax = row_max(s, f_cf);
-          const float m_new = tmax > m_run + kTau ? tmax : m_run;
+        if (__ballot(tmax > m_run + kTau) != 0ull) {
+          const float m_new = fmaxf(m_run, tmax);
           const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
           m_run = m_new;
           l_part *= alpha;
           factor *= alpha;
           scale_o = true;
-          lt = 0.0f;
-          softmax_weights(s, f_cf, m_run, lt, pb);
         }
-        l_part += lt;
         if (scale_o) {
-#pragma unroll
+  #pragma unroll
           for (int b = 0; b < DB; ++b)
-#pragma unroll
+  #pragma unroll
             for (int j = 0; j < 16; ++j) oacc[b][j] *= factor;
         }
+        softmax_weights(s, f_cf, m_run, l_part, pb);
       };
 
       // VALU phase of step t: softmax of tile t, then the queries turned into
