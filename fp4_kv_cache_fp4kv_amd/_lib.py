@@ -25,7 +25,7 @@ FP4KV_MAX_SLOTS = 64
 
 EXPORTED = ("fp4kv_strerror", "fp4kv_abi_version", "fp4kv_cache_nbytes", "fp4kv_cache_reset",
             "fp4kv_append_workspace_bytes", "fp4kv_quantize_append", "fp4kv_rope_table",
-            "fp4kv_rope_rel", "fp4kv_attention_chunk")
+            "fp4kv_rope_rel", "fp4kv_attention_chunk", "fp4kv_attention_set_workgroups")
 
 
 class CacheDesc(ctypes.Structure):
@@ -93,6 +93,8 @@ def load() -> ctypes.CDLL:
     lib.fp4kv_attention_chunk.argtypes = [P(CacheDesc), vp, c_int, vp, c_int, c_i32, c_i32,
                                           P(c_i32), vp, c_i32, c_f, vp]
     lib.fp4kv_attention_chunk.restype = c_int
+    lib.fp4kv_attention_set_workgroups.argtypes = [c_i32]
+    lib.fp4kv_attention_set_workgroups.restype = c_int
     _lib = lib
     return lib
 

@@ -178,6 +178,12 @@ def attention_chunk(cache: FP4KVCache, q_rot: torch.Tensor, q_frame0: int, n_q_f
     return out
 
 
+def set_attention_workgroups(n: int) -> None:
+    """fp4kv_attention_set_workgroups: split the attention work over n
+    workgroups (capped at the number of compute units); 0 = default."""
+    check(load().fp4kv_attention_set_workgroups(int(n)), "fp4kv_attention_set_workgroups")
+
+
 def cache_positions(S: int, W: int, f0: int, n: int) -> int:
     """Cache-relative position of the first query frame of a step (its
     pos0 for rope_rel): f0 if f0 < S, else S + f0 - max(S, f0 + n - W)."""

@@ -235,4 +235,10 @@ int fp4kv_attention_chunk(const fp4kv_cache *c, const void *q_rot, int q_dtype, 
   return from_hip(launch_attention(p, c->head_dim, out_dtype == FP4KV_F32, (hipStream_t)stream));
 }
 
+int fp4kv_attention_set_workgroups(int32_t n) {
+  if (n < 0) return FP4KV_EINVAL;
+  g_attention_workgroups.store(n);
+  return FP4KV_OK;
+}
+
 }  // extern "C"

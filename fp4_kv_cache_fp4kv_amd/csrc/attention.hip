@@ -7,26 +7,25 @@
 // together ...").
 //
 // Work layout (gfx950, wave64, MFMA 32x32x16 with f16 operands, f32 accum):
-//   * one workgroup = 128 query rows of one head, 4 waves x 32 rows, one
-//     workgroup per CU, so every wave owns a SIMD and up to 512 registers;
-//   * the keys of all visible frames are walked as one sequence of 64-key
-//     tiles.  Three LDS buffers hold dequantized tiles: while the waves
-//     compute with tiles t and t+1, the workgroup dequantizes tile t+2 from
-//     packed codes it loaded one tile earlier and loads the codes of tile
-//     t+3.  Dequantization is exact: E2M1 x E4M3 has at most 6 significant
-//     bits and lies in [2^-10, 2688], so it fits f16; the hardware converts
-//     two FP4 codes to f16 (scale 1) and one packed f16 multiply applies the
+//   * a row block is 256 query rows of one head, held by one workgroup of 8
+//     waves x 32 rows (one workgroup per CU, two waves per SIMD);
+//   * the keys of all visible frames of a row block are walked as one
+//     sequence of 64-key tiles, dequantized into LDS (2 K and 3 V buffers).
+//     Dequantization is exact: E2M1 x E4M3 has at most 6 significant bits
+//     and lies in [2^-10, 2688], so it fits f16; the hardware converts two
+//     FP4 codes to f16 (scale 1) and one packed f16 multiply applies the
 //     block scale;
 //   * each wave computes S^T = K Q^T so that a lane owns one query row in
 //     both the score and the output accumulators: the softmax row max and sum
 //     stay inside a lane plus one exchange with the lane 32 away;
 //   * O^T += V^T P^T, with P taken straight from the score registers and V
 //     read dimension-major, as the cache stores it;
-//   * software pipeline with one barrier per tile: the MFMAs of S(t+1) are
-//     issued together with the exp2 work of tile t, and the MFMAs of V(t) P(t)
-//     together with the dequantization of tile t+2, the loads of tile t+3
-//     and the mask and row max of S(t+1), so that the matrix core and the
-//     vector ALU of a SIMD are busy at the same time.
+//   * ping-pong schedule: the waves form two groups with one wave of each
+//     on every SIMD, and while one group issues MFMAs (with the dequantization
+//     of a later tile in their shadow) the other does the softmax;
+//   * split schedule: the key tiles of all row blocks are cut into one
+//     contiguous range per workgroup; a row block shared by two or more
+//     ranges is finished by a log-sum-exp merge of the pieces.
 //
 // Rotation: the cache holds keys before rotation.  Rotating q by pos(qf) and
 // k by pos(kf) gives the same score as rotating q by pos(qf) - pos(kf), so
@@ -42,6 +41,11 @@
 // changes.
 #include "fp4kv_device.hpp"
 #include "internal.hpp"
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
 
 namespace fp4kv {
 namespace {
@@ -62,6 +66,10 @@ constexpr int kKBufs = 2, kVBufs = 3;   // dequantized K and V tiles in LDS
 // offsets past the end return zero instead of touching memory.
 constexpr uint32_t kBufferWord3 = 0x00020000u;
 constexpr uint32_t kOutOfRange = 0x80000000u;
+// Cache-policy operand of the buffer intrinsics: sc1, a device-coherent access.
+constexpr int kSc1 = 16;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, (int)bytes,
                                            (int)kBufferWord3);
@@ -125,6 +133,8 @@ struct Smem {
   float fl_gk[FP4KV_MAX_SLOTS];
   float fl_gv[FP4KV_MAX_SLOTS];
   int n_fl;
+  int seg_c0, seg_c1;   // walk range [seg_c0, seg_c1) of the current segment
+  int merge_last;       // this workgroup completes the current row block
 };
 
 // Packed codes and scales held by one thread between the load and the
@@ -406,6 +416,36 @@ __device__ __forceinline__ void barrier_reads_in_flight() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// The kernel's argument block (a single AttnParams at offset 0), read
+// through a pointer the compiler cannot see through.
+__device__ __forceinline__ const AttnParams &opaque_params() {
+  auto kp = (const __attribute__((address_space(4))) AttnParams *)
+      __builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kp));
+  return *(const AttnParams *)kp;
+}
+
+// First virtual tile of workgroup w when n_units tiles are cut into n_wg
+// contiguous ranges of (nearly) equal length.
+__device__ __forceinline__ long long split_start(int w, long long n_units, int n_wg) {
+  return (long long)w * n_units / n_wg;
+}
+
+// Workgroup whose range holds virtual tile x: the largest w with
+// split_start(w) <= x.
+__device__ __forceinline__ int split_owner(long long x, long long n_units, int n_wg) {
+  return (int)(((x + 1) * n_wg + n_units - 1) / n_units) - 1;
+}
+
+// Index in a row block's walk (the tiles of its visible slots, in slot order)
+// of the first walked tile at or after virtual tile x = slot * n_tiles + tt.
+__device__ __forceinline__ int walk_index(unsigned long long visible, int x, int n_tiles) {
+  const int slot = x / n_tiles, tt = x - slot * n_tiles;
+  const unsigned long long below = slot >= 64 ? visible : visible & ((1ull << slot) - 1ull);
+  const bool here = slot < 64 && ((visible >> slot) & 1ull);
+  return __popcll(below) * n_tiles + (here ? tt : 0);
+}
+
 // Ping-pong schedule.  The 8 waves form two groups of 4 with one wave of
 // each group on every SIMD; both groups walk the same tiles for different
 // query rows, offset by one phase.  Phases end at workgroup barriers, and in
@@ -427,316 +467,501 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   Smem<D> &sm = *reinterpret_cast<Smem<D> *>(smem_raw);
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int n = lane & 31, hf = lane >> 5;
-  const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);
-  const int lt = tid & 255;   // thread index within the group
-  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-  // L2).  Give XCD x the contiguous work items [x*per, (x+1)*per) in
-  // head-major order, so each head's FP4 KV is read into few L2s.
   const int n_qt = (p.Nq + kBM - 1) / kBM;
-  const int n_work = n_qt * p.H;
-  const int per = (n_work + kXcds - 1) / kXcds;
-  const int work = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
-  if (work >= n_work) return;
-  const int head = work / n_qt;
-  const int f1 = p.q_frame0 + p.n_q_frames;
-  const int ws = max(p.S, f1 - p.W);
-
-  const int wg_row0 = (work - head * n_qt) * kBM;
-  const int my_row = wg_row0 + wave * 32 + n;
-  const bool row_ok = my_row < p.Nq;
-  const int my_qf = p.q_frame0 + (row_ok ? my_row : p.Nq - 1) / p.T;
-  const int my_qshot = p.q_shot[my_qf - p.q_frame0];
-  const int my_qchunk = my_qf / p.C;
-
-  // ---- visible key frames of this workgroup (one wave, ballot compaction)
-  if (wave == 0) {
-    const int qf_lo = p.q_frame0 + wg_row0 / p.T;
-    const int qf_hi = p.q_frame0 + (min(p.Nq, wg_row0 + kBM) - 1) / p.T;
-    bool ok = false;
-    int kf = -1, kshot = 0;
-    if (lane < p.n_slots) {
-      kf = p.slot_frame[lane];
-      kshot = p.slot_shot[lane];
-      ok = kf >= 0 && kf < f1 && (kf < p.S || kf >= ws);
-      if (ok) {
-        bool any = false;
-        for (int qf = qf_lo; qf <= qf_hi; ++qf)
-          any |= (kf / p.C <= qf / p.C) && (kf < p.S || kshot == p.q_shot[qf - p.q_frame0]);
-        ok = any;
-      }
-    }
-    const unsigned long long mask = __ballot(ok);
-    const int idx = __popcll(mask & ((1ull << lane) - 1ull));
-    if (ok) {
-      sm.fl_slot[idx] = lane;
-      sm.fl_kf[idx] = kf;
-      sm.fl_pos[idx] = kf < p.S ? kf : p.S + (kf - ws);
-      sm.fl_shot[idx] = kshot;
-      sm.fl_gk[idx] = p.k_tscale[lane];
-      sm.fl_gv[idx] = p.v_tscale[lane];
-    }
-    if (lane == 0) sm.n_fl = __popcll(mask);
-  }
-  __syncthreads();
-
-  const int n_fl = sm.n_fl;
   const int n_tiles = (p.Tc + kBN - 1) / kBN;
   const int last_nval = p.Tc - (n_tiles - 1) * kBN;
   const int half_rot = p.rot_dim >> 1;
+  const int f1 = p.q_frame0 + p.n_q_frames;
+  const int ws = max(p.S, f1 - p.W);
 
-  // ---- turn into listed frame fi: R(-(pos(fi) - pos(fi - 1))), pos(-1) = 0;
-  // pairs past rot_dim / 2 get the identity (1, 0)
-  for (int i = tid; i < n_fl * (D / 2); i += kThreads) {
-    const int fi = i / (D / 2), j = i % (D / 2);
-    const int dpos = sm.fl_pos[fi] - (fi > 0 ? sm.fl_pos[fi - 1] : 0);
-    float2 cs = make_float2(1.0f, 0.0f);
-    if (j < half_rot) {
-      const float2 t = *(const float2 *)(p.cos_sin + (long long)abs(dpos) * p.rot_dim + 2 * j);
-      cs = make_float2(t.x, dpos >= 0 ? -t.y : t.y);
+  // ---- split schedule.  A row block (kBM query rows of one head, head-major
+  // order) has n_v virtual tiles, n_tiles per cache slot; the n_wg
+  // workgroups take equal contiguous ranges of the virtual tiles of all row
+  // blocks.  Tiles of invisible slots cost nothing, so the ranges are
+  // balanced whenever the row blocks see the same frames.  A row block that
+  // lies inside one range is finished directly; the pieces of a row block
+  // shared by several ranges leave partial results (g_v * acc, m, l) in the
+  // workspace, and the workgroup that completes the row block last merges
+  // them.  Workgroups are dispatched round-robin over the 8 XCDs (each with
+  // its own L2): XCD x takes the contiguous ranges of workgroups
+  // [x*per, (x+1)*per), so each head's FP4 KV is read into few L2s.
+  const int per = (int)gridDim.x / kXcds;
+  const int w = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+  if (w >= p.n_wg) return;
+  const long long n_v = (long long)p.n_slots * n_tiles;
+  const long long n_units = (long long)n_qt * p.H * n_v;
+  const long long u0 = split_start(w, n_units, p.n_wg);
+  const long long u1 = split_start(w + 1, n_units, p.n_wg);
+  if (u0 >= u1) return;
+  const long long blk0 = u0 / n_v;
+  for (long long blk = blk0; blk * n_v < u1; ++blk) {
+    const long long vbase = blk * n_v;
+    const int v_lo = (int)(max(u0, vbase) - vbase), v_hi = (int)(min(u1, vbase + n_v) - vbase);
+    if (blk != blk0) __syncthreads();   // the previous row block's LDS is no longer read
+    // The kernel arguments and the thread index are made opaque in every
+    // segment, so that the compiler derives addresses and divisors here
+    // instead of holding them (spilled) across the segment loop.
+    const AttnParams &p = opaque_params();
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, hf = lane >> 5;
+    const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);
+    const int lt = tid & 255;   // thread index within the group
+    const int head = (int)(blk / n_qt);
+    const int wg_row0 = (int)(blk - (long long)head * n_qt) * kBM;
+    const int my_row = wg_row0 + wave * 32 + n;
+    const bool row_ok = my_row < p.Nq;
+    const int my_qf = p.q_frame0 + (row_ok ? my_row : p.Nq - 1) / p.T;
+    const int my_qshot = p.q_shot[my_qf - p.q_frame0];
+    const int my_qchunk = my_qf / p.C;
+
+    // ---- visible key frames of this workgroup (one wave, ballot compaction)
+    if (wave == 0) {
+      const int qf_lo = p.q_frame0 + wg_row0 / p.T;
+      const int qf_hi = p.q_frame0 + (min(p.Nq, wg_row0 + kBM) - 1) / p.T;
+      bool ok = false;
+      int kf = -1, kshot = 0;
+      if (lane < p.n_slots) {
+        kf = p.slot_frame[lane];
+        kshot = p.slot_shot[lane];
+        ok = kf >= 0 && kf < f1 && (kf < p.S || kf >= ws);
+        if (ok) {
+          bool any = false;
+          for (int qf = qf_lo; qf <= qf_hi; ++qf)
+            any |= (kf / p.C <= qf / p.C) && (kf < p.S || kshot == p.q_shot[qf - p.q_frame0]);
+          ok = any;
+        }
+      }
+      const unsigned long long mask = __ballot(ok);
+      const int idx = __popcll(mask & ((1ull << lane) - 1ull));
+      if (ok) {
+        sm.fl_slot[idx] = lane;
+        sm.fl_kf[idx] = kf;
+        sm.fl_pos[idx] = kf < p.S ? kf : p.S + (kf - ws);
+        sm.fl_shot[idx] = kshot;
+        sm.fl_gk[idx] = p.k_tscale[lane];
+        sm.fl_gv[idx] = p.v_tscale[lane];
+      }
+      if (lane == 0) {
+        sm.n_fl = __popcll(mask);
+        sm.seg_c0 = walk_index(mask, v_lo, n_tiles);
+        sm.seg_c1 = walk_index(mask, v_hi, n_tiles);
+      }
     }
-    sm.rot[fi][j] = cs;
-  }
+    __syncthreads();
 
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int b = 0; b < DB; ++b)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) oacc[b][j] = 0.0f;
-  float m_run = -1.0e30f, l_part = 0.0f, gv_last = 1.0f;
+    // The segment walks the tiles [c0, c0 + n_total) of the row block's walk,
+    // from tile ta of listed frame fa to tile te of listed frame fe.
+    const int c0 = sm.seg_c0, n_total = sm.seg_c1 - c0;
+    const int fa = c0 / n_tiles, ta = c0 - fa * n_tiles;
+    const int fe = (c0 + max(n_total, 1) - 1) / n_tiles, te = c0 + max(n_total, 1) - 1 - fe * n_tiles;
 
-  if (n_fl > 0) {
-    const int krow = krow_phys(sigma(n));   // + 32 b for key block b
-    const long long qoff = ((long long)(row_ok ? my_row : 0) * p.H + head) * D + 8 * hf;
-    const int n_total = n_fl * n_tiles;
-    f16x8 qhi[KS], qlo[KS];
+    // ---- turn into listed frame fi: R(-(pos(fi) - pos(fi - 1))), and
+    // R(-pos(fa)) into the segment's first frame; pairs past rot_dim / 2 get
+    // the identity (1, 0)
+    for (int i = tid; i < (n_total > 0 ? fe - fa + 1 : 0) * (D / 2); i += kThreads) {
+      const int fi = fa + i / (D / 2), j = i % (D / 2);
+      const int dpos = sm.fl_pos[fi] - (fi > fa ? sm.fl_pos[fi - 1] : 0);
+      float2 cs = make_float2(1.0f, 0.0f);
+      if (j < half_rot) {
+        const float2 t = *(const float2 *)(p.cos_sin + (long long)abs(dpos) * p.rot_dim + 2 * j);
+        cs = make_float2(t.x, dpos >= 0 ? -t.y : t.y);
+      }
+      sm.rot[fi][j] = cs;
+    }
 
-    // Turns the queries into listed frame fi: the first frame reads the
-    // rotated queries from memory, later frames turn the previous frame's.
-    auto turn_queries = [&](int fi, bool from_memory) __attribute__((always_inline)) {
-      const float2 *rot = sm.rot[fi];
+    f32x16 oacc[DB];
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        float x[8];
-        if (from_memory) {
-          if (p.q_f32) {
-            const float4 a = *(const float4 *)((const float *)p.q + qoff + 16 * kk);
-            const float4 b = *(const float4 *)((const float *)p.q + qoff + 16 * kk + 4);
-            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-            x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) oacc[b][j] = 0.0f;
+    float m_run = -1.0e30f, l_part = 0.0f, gv_last = 1.0f;
+
+    if (n_total > 0) {
+      const int krow = krow_phys(sigma(n));   // + 32 b for key block b
+      const long long qoff = ((long long)(row_ok ? my_row : 0) * p.H + head) * D + 8 * hf;
+      f16x8 qhi[KS], qlo[KS];
+
+      // Turns the queries into listed frame fi: the first frame reads the
+      // rotated queries from memory, later frames turn the previous frame's.
+      auto turn_queries = [&](int fi, bool from_memory) __attribute__((always_inline)) {
+        const float2 *rot = sm.rot[fi];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          float x[8];
+          if (from_memory) {
+            if (p.q_f32) {
+              const float4 a = *(const float4 *)((const float *)p.q + qoff + 16 * kk);
+              const float4 b = *(const float4 *)((const float *)p.q + qoff + 16 * kk + 4);
+              x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+              x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+            } else {
+              const uint4 v = *(const uint4 *)((const uint16_t *)p.q + qoff + 16 * kk);
+              const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                x[2 * e] = __uint_as_float(w[e] << 16);
+                x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = row_ok ? x[e] : 0.0f;
           } else {
-            const uint4 v = *(const uint4 *)((const uint16_t *)p.q + qoff + 16 * kk);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              x[2 * e] = __uint_as_float(w[e] << 16);
-              x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+            for (int e = 0; e < 8; ++e) x[e] = (float)qhi[kk][e] + (float)qlo[kk][e];
+          }
+          uint32_t hw[4], lw[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float2 cs = rot[8 * kk + 4 * hf + e];
+            float ra, rb;
+            rotate_pair(x[2 * e], x[2 * e + 1], cs.x, cs.y, ra, rb);
+            const f16x2 h2 = {(_Float16)ra, (_Float16)rb};
+            const f16x2 l2 = {(_Float16)(ra - (float)h2[0]), (_Float16)(rb - (float)h2[1])};
+            hw[e] = bits(h2);
+            lw[e] = bits(l2);
+          }
+          qhi[kk] = as_f16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+          qlo[kk] = as_f16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        }
+      };
+
+      // Next tile of the walk (the segment's last tile stays put).
+      auto advance = [&](Cursor c) __attribute__((always_inline)) {
+        if (c.fi == fe && c.tt == te) return c;
+        ++c.i;
+        if (++c.tt == n_tiles) {
+          c.tt = 0;
+          ++c.fi;
+        }
+        return c;
+      };
+      // Per-frame values of the frame of the tile whose softmax comes next:
+      // visibility of this lane's row, whether the whole wave sees the frame,
+      // the exp2 factor softmax_scale * log2(e) * g_k and the value scale g_v.
+      // f_ratio = g_v(previous frame) / g_v(this frame) keeps O = g_v * acc.
+      bool f_vis = false, f_all = false;
+      float f_cf = 0.0f, f_gv = 1.0f, f_ratio = 1.0f;
+      auto load_frame = [&](int fi) __attribute__((always_inline)) {
+        const int kf = sm.fl_kf[fi];
+        f_vis = row_ok & (kf / p.C <= my_qchunk) & ((kf < p.S) | (sm.fl_shot[fi] == my_qshot));
+        f_all = __ballot(f_vis) == ~0ull;
+        f_cf = p.scale_log2 * sm.fl_gk[fi];
+        const float gv = sm.fl_gv[fi];
+        f_ratio = __fdiv_rn(f_gv, gv);
+        f_gv = gv;
+      };
+
+      // Each group dequantizes one half (group 0: V, group 1: K) of the tiles
+      // in walk order; cd is the next tile whose codes are loaded or loading.
+      // The two groups run the same walk; group 1 dequantizes K halves and
+      // group 0 V halves, so each group's code holds only its own codes.
+      // L: the wave has query rows below Nq.  A wave past the last row (in
+      // the ragged last row block of a head) skips its MFMAs and softmax and
+      // only dequantizes its share of the tiles.
+      auto run_group = [&](auto gtag, auto ltag) __attribute__((always_inline)) {
+        constexpr bool G = decltype(gtag)::value;
+        constexpr bool L = decltype(ltag)::value;
+        typename RawOf<G>::type raw;
+        Cursor cd = {fa, ta, 0};
+        SlotRes res = slot_resources<D>(p, head, sm.fl_slot[fa]);   // frame of cd
+        auto load_half = [&]() __attribute__((always_inline)) {
+          if constexpr (G) load_k<D>(res, cd.tt * kBN, lt, raw);
+          else load_v<D>(res, p.Tv, cd.tt * kBN, lt, raw);
+        };
+        // Dequantizes the half tile cd.i into its buffer and loads the codes of
+        // the next one.  Past the end of the walk the loads repeat the last
+        // tile and the dequantized copies land in buffers no phase reads.
+        auto dequant_next = [&]() __attribute__((always_inline)) {
+          if constexpr (G) dequant_k<D>(raw, lt, sm.kh[cd.i % kKBufs]);
+          else dequant_v<D>(raw, lt, sm.vt[cd.i % kVBufs]);
+          Cursor nx = advance(cd);
+          nx.i = cd.i + 1;
+          if (nx.fi != cd.fi) res = slot_resources<D>(p, head, sm.fl_slot[nx.fi]);
+          cd = nx;
+          load_half();
+        };
+
+        // ---- prologue: tile 0 dequantized, the codes of tile 1 loading
+        load_half();
+        dequant_next();
+        lds_barrier();   // tile 0, the turn table and the frame list are in LDS
+
+        if constexpr (L) turn_queries(fa, true);
+        load_frame(fa);
+        Cursor ct = {fa, ta, 0};   // tile of this group's next S and softmax
+        f32x16 s[2];
+        f16x8 pb[4];
+        f16x8 va[D / 8];   // V operands of the tile whose PV comes next
+
+        // Softmax of tile t (ct): mask, row max, lazy rescale of O and l
+        // together with the g_v ratio on the first tile of a frame, then P and l.
+        auto softmax_tile = [&](auto masked) __attribute__((always_inline)) {
+          const int nval = ct.tt == n_tiles - 1 ? last_nval : kBN;
+          const float tmax = mask_and_max<decltype(masked)::value>(s, f_vis, nval, hf, f_cf);
+          const bool first = ct.i > 0 && ct.tt == 0;
+          float factor = first ? f_ratio : 1.0f;
+          bool scale_o = first;
+          if (__ballot(tmax > m_run + kTau) != 0ull) {
+            const float m_new = fmaxf(m_run, tmax);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_part *= alpha;
+            factor *= alpha;
+            scale_o = true;
+          }
+          if (scale_o) {
+    #pragma unroll
+            for (int b = 0; b < DB; ++b)
+    #pragma unroll
+              for (int j = 0; j < 16; ++j) oacc[b][j] *= factor;
+          }
+          softmax_weights(s, f_cf, m_run, l_part, pb);
+        };
+
+        // VALU phase of step t: softmax of tile t, then the queries turned into
+        // the frame of tile t+1
+        auto valu_phase = [&](int t) __attribute__((always_inline)) {
+          if constexpr (L) {
+            if (t < n_total) {
+              if (!f_all || (ct.tt == n_tiles - 1 && last_nval < kBN))
+                softmax_tile(BoolC<true>());
+              else
+                softmax_tile(BoolC<false>());
             }
           }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = row_ok ? x[e] : 0.0f;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = (float)qhi[kk][e] + (float)qlo[kk][e];
-        }
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float2 cs = rot[8 * kk + 4 * hf + e];
-          float ra, rb;
-          rotate_pair(x[2 * e], x[2 * e + 1], cs.x, cs.y, ra, rb);
-          const f16x2 h2 = {(_Float16)ra, (_Float16)rb};
-          const f16x2 l2 = {(_Float16)(ra - (float)h2[0]), (_Float16)(rb - (float)h2[1])};
-          hw[e] = bits(h2);
-          lw[e] = bits(l2);
-        }
-        qhi[kk] = as_f16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-        qlo[kk] = as_f16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
-      }
-    };
-
-    // Next tile of the walk (the last tile stays put).
-    auto advance = [&](Cursor c) __attribute__((always_inline)) {
-      if (c.fi == n_fl - 1 && c.tt == n_tiles - 1) return c;
-      ++c.i;
-      if (++c.tt == n_tiles) {
-        c.tt = 0;
-        ++c.fi;
-      }
-      return c;
-    };
-    // Per-frame values of the frame of the tile whose softmax comes next:
-    // visibility of this lane's row, whether the whole wave sees the frame,
-    // the exp2 factor softmax_scale * log2(e) * g_k and the value scale g_v.
-    // f_ratio = g_v(previous frame) / g_v(this frame) keeps O = g_v * acc.
-    bool f_vis = false, f_all = false;
-    float f_cf = 0.0f, f_gv = 1.0f, f_ratio = 1.0f;
-    auto load_frame = [&](int fi) __attribute__((always_inline)) {
-      const int kf = sm.fl_kf[fi];
-      f_vis = row_ok & (kf / p.C <= my_qchunk) & ((kf < p.S) | (sm.fl_shot[fi] == my_qshot));
-      f_all = __ballot(f_vis) == ~0ull;
-      f_cf = p.scale_log2 * sm.fl_gk[fi];
-      const float gv = sm.fl_gv[fi];
-      f_ratio = __fdiv_rn(f_gv, gv);
-      f_gv = gv;
-    };
-
-    // Each group dequantizes one half (group 0: V, group 1: K) of the tiles
-    // in walk order; cd is the next tile whose codes are loaded or loading.
-    // The two groups run the same walk; group 1 dequantizes K halves and
-    // group 0 V halves, so each group's code holds only its own codes.
-    auto run_group = [&](auto gtag) __attribute__((always_inline)) {
-      constexpr bool G = decltype(gtag)::value;
-      typename RawOf<G>::type raw;
-      Cursor cd = {0, 0, 0};
-      SlotRes res = slot_resources<D>(p, head, sm.fl_slot[0]);   // frame of cd
-      auto load_half = [&]() __attribute__((always_inline)) {
-        if constexpr (G) load_k<D>(res, cd.tt * kBN, lt, raw);
-        else load_v<D>(res, p.Tv, cd.tt * kBN, lt, raw);
-      };
-      // Dequantizes the half tile cd.i into its buffer and loads the codes of
-      // the next one.  Past the end of the walk the loads repeat the last
-      // tile and the dequantized copies land in buffers no phase reads.
-      auto dequant_next = [&]() __attribute__((always_inline)) {
-        if constexpr (G) dequant_k<D>(raw, lt, sm.kh[cd.i % kKBufs]);
-        else dequant_v<D>(raw, lt, sm.vt[cd.i % kVBufs]);
-        Cursor nx = advance(cd);
-        nx.i = cd.i + 1;
-        if (nx.fi != cd.fi) res = slot_resources<D>(p, head, sm.fl_slot[nx.fi]);
-        cd = nx;
-        load_half();
-      };
-
-      // ---- prologue: tile 0 dequantized, the codes of tile 1 loading
-      load_half();
-      dequant_next();
-      lds_barrier();   // tile 0, the turn table and the frame list are in LDS
-
-      turn_queries(0, true);
-      load_frame(0);
-      Cursor ct = {0, 0, 0};   // tile of this group's next S and softmax
-      f32x16 s[2];
-      f16x8 pb[4];
-      f16x8 va[D / 8];   // V operands of the tile whose PV comes next
-
-      // Softmax of tile t (ct): mask, row max, lazy rescale of O and l
-      // together with the g_v ratio on the first tile of a frame, then P and l.
-      auto softmax_tile = [&](auto masked) __attribute__((always_inline)) {
-        const int nval = ct.tt == n_tiles - 1 ? last_nval : kBN;
-        const float tmax = mask_and_max<decltype(masked)::value>(s, f_vis, nval, hf, f_cf);
-        const bool first = ct.i > 0 && ct.tt == 0;
-        float factor = first ? f_ratio : 1.0f;
-        bool scale_o = first;
-        if (__ballot(tmax > m_run + kTau) != 0ull) {
-          const float m_new = fmaxf(m_run, tmax);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-          m_run = m_new;
-          l_part *= alpha;
-          factor *= alpha;
-          scale_o = true;
-        }
-        if (scale_o) {
-  #pragma unroll
-          for (int b = 0; b < DB; ++b)
-  #pragma unroll
-            for (int j = 0; j < 16; ++j) oacc[b][j] *= factor;
-        }
-        softmax_weights(s, f_cf, m_run, l_part, pb);
-      };
-
-      // VALU phase of step t: softmax of tile t, then the queries turned into
-      // the frame of tile t+1
-      auto valu_phase = [&](int t) __attribute__((always_inline)) {
-        if (t < n_total) {
-          if (!f_all || (ct.tt == n_tiles - 1 && last_nval < kBN))
-            softmax_tile(BoolC<true>());
-          else
-            softmax_tile(BoolC<false>());
-        }
-        if (t + 1 < n_total) {
-          const Cursor cn = advance(ct);
-          if (cn.fi != ct.fi) {
-            turn_queries(cn.fi, false);
-            load_frame(cn.fi);
+          if (t + 1 < n_total) {
+            const Cursor cn = advance(ct);
+            if (cn.fi != ct.fi) {
+              if constexpr (L) turn_queries(cn.fi, false);
+              load_frame(cn.fi);
+            }
+            ct = cn;
           }
-          ct = cn;
-        }
-        // V operands of tile t for the next MFMA phase (V(t) has been in LDS
-        // since phase 2t-2 and is overwritten only in phase 2t+4)
-        read_v_operands<D>(va, sm.vt[t % kVBufs], n, hf);
-      };
+          // V operands of tile t for the next MFMA phase (V(t) has been in LDS
+          // since phase 2t-2 and is overwritten only in phase 2t+4)
+          if constexpr (L) read_v_operands<D>(va, sm.vt[t % kVBufs], n, hf);
+        };
 
-      // MFMA phase of step t, with the dequantization of the group's next
-      // half tile in the shadow of the MFMAs.  P is consumed first and S
-      // produced last, which keeps the registers of P, the dequantization and
-      // S from being live at the same time.
-      auto mfma_phase = [&](int t, auto has_pv, auto has_s) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_setprio(1);
-        if constexpr (decltype(has_pv)::value) accumulate_pv<D>(oacc, va, pb);
-        dequant_next();
-        if constexpr (decltype(has_s)::value)
-          scores<D>(s, sm.kh[t % kKBufs], krow, hf, qhi, qlo);
-        __builtin_amdgcn_s_setprio(0);
-        lds_barrier();
-      };
+        // MFMA phase of step t, with the dequantization of the group's next
+        // half tile in the shadow of the MFMAs.  P is consumed first and S
+        // produced last, which keeps the registers of P, the dequantization and
+        // S from being live at the same time.
+        auto mfma_phase = [&](int t, auto has_pv, auto has_s) __attribute__((always_inline)) {
+          __builtin_amdgcn_s_setprio(1);
+          if constexpr (L && decltype(has_pv)::value) accumulate_pv<D>(oacc, va, pb);
+          dequant_next();
+          if constexpr (L && decltype(has_s)::value)
+            scores<D>(s, sm.kh[t % kKBufs], krow, hf, qhi, qlo);
+          __builtin_amdgcn_s_setprio(0);
+          lds_barrier();
+        };
 
-      if (G) lds_barrier();   // group 1's opening phase
-      mfma_phase(0, BoolC<false>(), BoolC<true>());
-      valu_phase(0);
-      barrier_reads_in_flight();
-      for (int t = 1; t < n_total; ++t) {
-        mfma_phase(t, BoolC<true>(), BoolC<true>());
-        valu_phase(t);
+        if (G) lds_barrier();   // group 1's opening phase
+        mfma_phase(0, BoolC<false>(), BoolC<true>());
+        valu_phase(0);
         barrier_reads_in_flight();
-      }
-      mfma_phase(n_total, BoolC<true>(), BoolC<false>());
-      if (!G) lds_barrier();   // group 0's closing phase
-      gv_last = f_gv;
-    };
-    if (grp) run_group(BoolC<true>());
-    else run_group(BoolC<false>());
-  }
-
-  // ---- epilogue: O = g_v * acc / l, g_v of the last frame walked
-  const float l = halves_sum(l_part);
-  const float inv = l > 0.0f ? __fdiv_rn(gv_last, l) : 0.0f;
-  if (!row_ok) return;
-  const long long obase = ((long long)my_row * p.H + head) * D;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = 32 * db + 8 * i + 4 * hf;
-      const float v0 = oacc[db][4 * i] * inv, v1 = oacc[db][4 * i + 1] * inv;
-      const float v2 = oacc[db][4 * i + 2] * inv, v3 = oacc[db][4 * i + 3] * inv;
-      if (OUT_F32) {
-        *(float4 *)((float *)p.o + obase + d) = make_float4(v0, v1, v2, v3);
+        for (int t = 1; t < n_total; ++t) {
+          mfma_phase(t, BoolC<true>(), BoolC<true>());
+          valu_phase(t);
+          barrier_reads_in_flight();
+        }
+        mfma_phase(n_total, BoolC<true>(), BoolC<false>());
+        if (!G) lds_barrier();   // group 0's closing phase
+        gv_last = f_gv;
+      };
+      const bool live = wg_row0 + wave * 32 < p.Nq;   // wave-uniform
+      if (grp) {
+        if (live) run_group(BoolC<true>(), BoolC<true>());
+        else run_group(BoolC<true>(), BoolC<false>());
       } else {
-        const uint32_t w0 = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
-        const uint32_t w1 = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
-        *(uint2 *)((uint16_t *)p.o + obase + d) = make_uint2(w0, w1);
+        if (live) run_group(BoolC<false>(), BoolC<true>());
+        else run_group(BoolC<false>(), BoolC<false>());
       }
     }
+
+    // ---- epilogue: O = g_v * acc / l, g_v of the last frame walked
+    const float l = halves_sum(l_part);
+    auto store_out = [&](float inv) __attribute__((always_inline)) {
+      if (!row_ok) return;
+      const long long obase = ((long long)my_row * p.H + head) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 32 * db + 8 * i + 4 * hf;
+          const float v0 = oacc[db][4 * i] * inv, v1 = oacc[db][4 * i + 1] * inv;
+          const float v2 = oacc[db][4 * i + 2] * inv, v3 = oacc[db][4 * i + 3] * inv;
+          if (OUT_F32) {
+            *(float4 *)((float *)p.o + obase + d) = make_float4(v0, v1, v2, v3);
+          } else {
+            const uint32_t w0 = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+            const uint32_t w1 = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
+            *(uint2 *)((uint16_t *)p.o + obase + d) = make_uint2(w0, w1);
+          }
+        }
+    };
+    if (v_lo == 0 && v_hi == n_v) {   // the whole row block
+      store_out(l > 0.0f ? __fdiv_rn(gv_last, l) : 0.0f);
+      continue;
+    }
+
+    // ---- a piece of a shared row block: publish (g_v * acc, m, l) in the
+    // workgroup's first or second partial slot, then count the piece in.
+    // Pieces are written and read with device-coherent (sc1) accesses, which
+    // do not stop in an XCD's L2, so no L2 writeback or invalidation is
+    // needed between workgroups on different XCDs.
+    const int row = wave * 32 + n;
+    const __amdgpu_buffer_rsrc_t ws_o =
+        rsrc((const uint8_t *)p.ws_o, (uint32_t)(2 * p.n_wg * kBM * D * 4));
+    const __amdgpu_buffer_rsrc_t ws_ml =
+        rsrc((const uint8_t *)p.ws_ml, (uint32_t)(2 * p.n_wg * kBM * 8));
+    {
+      const int slot = blk == blk0 ? 2 * w : 2 * w + 1;
+      const int ob = ((slot * kBM + row) * D + 4 * hf) * 4;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            oacc[db][4 * i + e] *= gv_last;
+            x[e] = __float_as_uint(oacc[db][4 * i + e]);
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(x, ws_o, ob + (32 * db + 8 * i) * 4, 0, kSc1);
+        }
+      if (hf == 0) {
+        const u32x2 ml = {__float_as_uint(m_run), __float_as_uint(l)};
+        __builtin_amdgcn_raw_buffer_store_b64(ml, ws_ml, (slot * kBM + row) * 8, 0, kSc1);
+      }
+    }
+    const int w_first = split_owner(vbase, n_units, p.n_wg);
+    const int w_last = split_owner(vbase + n_v - 1, n_units, p.n_wg);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the piece is written
+    __syncthreads();
+    if (tid == 0)
+      sm.merge_last = __hip_atomic_fetch_add(p.ws_cnt + w_first, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) == w_last - w_first;
+    __syncthreads();
+    if (!sm.merge_last) continue;
+    if (tid == 0)   // ready for the next launch
+      __hip_atomic_store(p.ws_cnt + w_first, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // ---- the last piece in: log-sum-exp merge of all pieces of the row
+    // block, its own included, in workgroup order (so the result does not
+    // depend on which workgroup came last)
+    float m_all = -1.0e30f, l_all = 0.0f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) oacc[db][j] = 0.0f;
+    for (int wc = w_first; wc <= w_last; ++wc) {
+      const int slot = 2 * wc + (split_start(wc, n_units, p.n_wg) < vbase ? 1 : 0);
+      const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(ws_ml, (slot * kBM + row) * 8, 0, kSc1);
+      const float m_in = __uint_as_float(ml[0]), l_in = __uint_as_float(ml[1]);
+      const float m_new = fmaxf(m_all, m_in);
+      const float a_old = __builtin_amdgcn_exp2f(m_all - m_new);
+      const float a_in = __builtin_amdgcn_exp2f(m_in - m_new);
+      m_all = m_new;
+      l_all = l_all * a_old + l_in * a_in;
+      const int ib = ((slot * kBM + row) * D + 4 * hf) * 4;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 x =
+              __builtin_amdgcn_raw_buffer_load_b128(ws_o, ib + (32 * db + 8 * i) * 4, 0, kSc1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            oacc[db][4 * i + e] = oacc[db][4 * i + e] * a_old + __uint_as_float(x[e]) * a_in;
+        }
+    }
+    store_out(l_all > 0.0f ? __fdiv_rn(1.0f, l_all) : 0.0f);
+  }
+}
+
+constexpr int kMinPiece = 4;   // fewest virtual tiles per workgroup range
+
+struct SplitWs {
+  float *o = nullptr;
+  float2 *ml = nullptr;
+  int *cnt = nullptr;
+};
+
+// Workspace of the split schedule, one per (device, stream) so that launches
+// on different streams never share it, sized for max_wg workgroups at head
+// dimension 128.  Allocated on first use (the counters are zeroed and the
+// device synchronized once) and kept until the process ends.
+hipError_t split_workspace(int dev, hipStream_t s, int max_wg, SplitWs &out) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, SplitWs> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = cache.find({dev, s});
+  if (it != cache.end()) {
+    out = it->second;
+    return hipSuccess;
+  }
+  const size_t n_o = (size_t)2 * max_wg * kBM * 128, n_ml = (size_t)2 * max_wg * kBM;
+  const size_t bytes = n_o * sizeof(float) + n_ml * sizeof(float2) + (size_t)max_wg * sizeof(int);
+  void *buf = nullptr;
+  hipError_t e = hipMalloc(&buf, bytes);
+  if (e != hipSuccess) return e;
+  SplitWs ws;
+  ws.o = (float *)buf;
+  ws.ml = (float2 *)(ws.o + n_o);
+  ws.cnt = (int *)(ws.ml + n_ml);
+  e = hipMemset(ws.cnt, 0, (size_t)max_wg * sizeof(int));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(buf);
+    return e;
+  }
+  cache[{dev, s}] = ws;
+  out = ws;
+  return hipSuccess;
 }
 
 template <int D, bool OUT_F32>
-hipError_t launch_one(const AttnParams &p, hipStream_t s) {
+hipError_t launch_one(AttnParams &p, hipStream_t s) {
   constexpr size_t bytes = smem_bytes<D>();
   static const hipError_t attr = hipFuncSetAttribute(
       (const void *)attention_kernel<D, OUT_F32>, hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)bytes);
   if (attr != hipSuccess) return attr;
-  const int n_work = (p.Nq + kBM - 1) / kBM * p.H;
-  const dim3 grid((n_work + kXcds - 1) / kXcds * kXcds);
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  // One workgroup per CU (one fits a CU), each range at least kMinPiece
+  // virtual tiles long: a few row blocks are spread over all CUs, and a
+  // count that is not a multiple of the CUs is balanced instead of leaving a
+  // partial last round.
+  const long long n_rb = (long long)((p.Nq + kBM - 1) / kBM) * p.H;
+  const long long n_v = (long long)p.n_slots * ((p.Tc + kBN - 1) / kBN);
+  long long n_wg = std::min<long long>(cus, std::max<long long>(1, n_rb * n_v / kMinPiece));
+  const int forced = g_attention_workgroups.load();
+  if (forced > 0) n_wg = std::min(forced, cus);
+  n_wg = std::min(n_wg, n_rb * n_v);   // no empty range
+  p.n_wg = (int)n_wg;
+  if (n_rb % n_wg != 0) {   // some row blocks are shared between workgroups
+    SplitWs ws;
+    if ((e = split_workspace(dev, s, cus, ws)) != hipSuccess) return e;
+    p.ws_o = ws.o;
+    p.ws_ml = ws.ml;
+    p.ws_cnt = ws.cnt;
+  }
+  const dim3 grid((unsigned)((n_wg + kXcds - 1) / kXcds * kXcds));
   hipLaunchKernelGGL((attention_kernel<D, OUT_F32>), grid, dim3(kThreads), bytes, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attention(const AttnParams &p, int head_dim, int out_f32, hipStream_t s) {
+std::atomic<int> g_attention_workgroups{0};
+
+hipError_t launch_attention(AttnParams &p, int head_dim, int out_f32, hipStream_t s) {
   if (head_dim == 128) return out_f32 ? launch_one<128, true>(p, s) : launch_one<128, false>(p, s);
   return out_f32 ? launch_one<64, true>(p, s) : launch_one<64, false>(p, s);
 }

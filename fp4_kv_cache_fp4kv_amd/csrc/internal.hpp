@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fp4kv.h"
 
 namespace fp4kv {
@@ -47,12 +49,20 @@ struct AttnParams {
   int H, T, Tc, Tv, C, S, W, n_slots, rot_dim;
   int q_frame0, n_q_frames, Nq, q_f32;
   float scale_log2;        // softmax_scale * log2(e)
+  int n_wg;                // workgroups of the split schedule
+  float *ws_o;             // partial g_v * acc [2 n_wg][256 rows][D]
+  float2 *ws_ml;           // partial (m, l) [2 n_wg][256 rows]
+  int *ws_cnt;             // pieces counted in per row block [n_wg], zero between launches
   int32_t q_shot[FP4KV_MAX_FRAMES];
 };
 
 hipError_t launch_cache_reset(const fp4kv_cache &c, hipStream_t s);
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
 hipError_t launch_rope(const RopeParams &p, hipStream_t s);
-hipError_t launch_attention(const AttnParams &p, int head_dim, int out_f32, hipStream_t s);
+// Fills n_wg and the workspace pointers of p, then launches.
+hipError_t launch_attention(AttnParams &p, int head_dim, int out_f32, hipStream_t s);
+
+// Workgroups of the attention split schedule: 0 = one per compute unit.
+extern std::atomic<int> g_attention_workgroups;
 
 }  // namespace fp4kv

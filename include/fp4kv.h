@@ -237,11 +237,30 @@ int fp4kv_rope_rel(const void *x, int in_dtype, void *y, int out_dtype, int64_t 
  *   cos_sin device rotary table with n_pos >= S + W rows (fp4kv_rope_table,
  *           cache->rot_dim).
  * Rows with no visible key are written as zeros.
+ *
+ * Work split: the key tiles of all (256-row block, head) pairs are cut into
+ * one contiguous range per workgroup (by default one workgroup per compute
+ * unit).  A row block shared by two or more ranges is merged from partial
+ * results (log-sum-exp combine).  That needs a workspace, which the library
+ * allocates on the first such call on each (device, stream) pair: about
+ * 68 MB on a 256-CU device (hipMalloc, then one device synchronization), kept
+ * until the process ends.  Make that first call outside stream capture.
+ * Calls on one stream are ordered; calls on different streams use different
+ * workspaces.
  */
 int fp4kv_attention_chunk(const fp4kv_cache *c, const void *q_rot, int q_dtype, void *o,
                           int out_dtype, int32_t q_frame0, int32_t n_q_frames,
                           const int32_t *q_shot, const float *cos_sin,
                           int32_t n_pos, float softmax_scale, void *stream);
+
+/*
+ * fp4kv_attention_set_workgroups - number of workgroups the attention work is
+ * split over, for tuning and tests: n > 0 uses min(n, compute units), 0
+ * restores the default (one per compute unit, each with at least 4 key
+ * tiles).  Process-wide; affects later fp4kv_attention_chunk calls.
+ * Returns FP4KV_EINVAL for n < 0.
+ */
+int fp4kv_attention_set_workgroups(int32_t n);
 
 #ifdef __cplusplus
 }

@@ -64,6 +64,13 @@ def test_strerror_and_version():
     assert lib.fp4kv_append_workspace_bytes() >= 64
 
 
+def test_attention_workgroup_knob():
+    lib = _lib.load()
+    assert lib.fp4kv_attention_set_workgroups(-1) == _lib.FP4KV_EINVAL
+    assert lib.fp4kv_attention_set_workgroups(7) == 0
+    assert lib.fp4kv_attention_set_workgroups(0) == 0
+
+
 def test_cache_nbytes():
     lib = _lib.load()
     out = (ctypes.c_size_t * 6)()

@@ -136,6 +136,59 @@ def test_attention_empty_cache_gives_zeros():
     assert torch.count_nonzero(o).item() == 0
 
 
+@pytest.fixture
+def workgroups():
+    from fp4_kv_cache_fp4kv_amd import api
+    yield api.set_attention_workgroups
+    api.set_attention_workgroups(0)
+
+
+# 4 row blocks of 300 rows x 2 heads, 14 key tiles each at a full window
+# (7 slots x 2 tiles, the second ragged): 1 workgroup takes every row block
+# whole; 3, 5 and 13 workgroups cut row blocks into 2 to 4 merged pieces.
+@pytest.mark.parametrize("n_wg", [1, 3, 5, 13])
+def test_attention_split_schedules(n_wg, workgroups):
+    workgroups(n_wg)
+    w = wl.Workload("split", H=2, D=128, T=100, C=3, S=1, W=6, n_frames=15, seed=24,
+                    outlier_p=0.01, outlier_scale=20.0)
+    _run_stream(w, [1, 4])
+
+
+@pytest.mark.parametrize("n_wg", [2, 7])
+def test_attention_split_multishot_d64(n_wg, workgroups):
+    workgroups(n_wg)
+    w = wl.Workload("tiny_mix", H=3, D=64, T=24, C=3, S=2, W=6, n_frames=20, seed=21,
+                    dtype="bf16", token_stride=2, shot_len=5)
+    _run_stream(w, list(range(w.n_chunks)))
+
+
+def test_attention_split_is_deterministic(workgroups):
+    """Merged pieces are combined in a fixed order: repeated calls give the
+    same bytes, whichever workgroup finishes a row block last."""
+    from fp4_kv_cache_fp4kv_amd import api
+    workgroups(13)
+    w = wl.Workload("split", H=2, D=128, T=100, C=3, S=1, W=6, n_frames=15, seed=24,
+                    outlier_p=0.01, outlier_scale=20.0)
+    gc = gpu_cache(w)
+    for c in range(3):
+        f0, n = w.chunk_frames(c)
+        (q, qb), (k, kb), (v, vb) = step_inputs(w, c)
+        outs = [_gpu_step(api, gc, w, c, q, qb, k, kb, v, vb, append=(i == 0))
+                for i in range(3)]
+        assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_attention_split_empty_cache_gives_zeros(workgroups):
+    from fp4_kv_cache_fp4kv_amd import api
+    workgroups(3)
+    w = wl.TINY
+    gc = gpu_cache(w)
+    q = torch.randn(2 * w.T, w.H, w.D, device="cuda:0").bfloat16()
+    o = api.attention_chunk(gc, q, 0, 2, [0, 0], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o).item() == 0
+
+
 _FULL_ROWS = None
 
 
