@@ -21,11 +21,12 @@ FP4KV_F32 = 0
 FP4KV_BF16 = 1
 FP4KV_FORMAT_NVFP4_V1 = 0x3146564E
 FP4KV_MAX_FRAMES = 64
+FP4KV_MAX_WORKGROUPS = 4096
 FP4KV_MAX_SLOTS = 64
 
 EXPORTED = ("fp4kv_strerror", "fp4kv_abi_version", "fp4kv_cache_nbytes", "fp4kv_cache_reset",
             "fp4kv_append_workspace_bytes", "fp4kv_quantize_append", "fp4kv_rope_table",
-            "fp4kv_rope_rel", "fp4kv_attention_chunk", "fp4kv_attention_set_workgroups")
+            "fp4kv_rope_rel", "fp4kv_attention_chunk", "fp4kv_attention_workspace_bytes")
 
 
 class CacheDesc(ctypes.Structure):
@@ -91,10 +92,11 @@ def load() -> ctypes.CDLL:
                                    c_i32, vp, c_i32, vp]
     lib.fp4kv_rope_rel.restype = c_int
     lib.fp4kv_attention_chunk.argtypes = [P(CacheDesc), vp, c_int, vp, c_int, c_i32, c_i32,
-                                          P(c_i32), vp, c_i32, c_f, vp]
+                                          P(c_i32), vp, c_i32, c_f, c_i32, vp, ctypes.c_size_t,
+                                          vp]
     lib.fp4kv_attention_chunk.restype = c_int
-    lib.fp4kv_attention_set_workgroups.argtypes = [c_i32]
-    lib.fp4kv_attention_set_workgroups.restype = c_int
+    lib.fp4kv_attention_workspace_bytes.argtypes = [c_i32, c_i32]
+    lib.fp4kv_attention_workspace_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 

@@ -80,6 +80,13 @@ class FP4KVCache:
             setattr(self.desc, name, getattr(self, name).data_ptr())
         self.workspace = torch.zeros(lib.fp4kv_append_workspace_bytes(), dtype=torch.uint8,
                                      device=dev)
+        # attention workspace for up to one workgroup per compute unit,
+        # zero-filled once as the library requires
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        self.attn_workgroups = min(cus, _lib.FP4KV_MAX_WORKGROUPS)
+        self.attn_workspace = torch.zeros(
+            lib.fp4kv_attention_workspace_bytes(D, self.attn_workgroups), dtype=torch.uint8,
+            device=dev)
         table = rope_table(n, self.rot_dim) if self.rot_dim > 0 else torch.zeros(2)
         self.cos_sin = table.to(dev)
         self.n_pos = n
@@ -156,9 +163,13 @@ def rope_rel(x: torch.Tensor, pos0: int, tokens_per_frame: int, cos_sin: torch.T
 def attention_chunk(cache: FP4KVCache, q_rot: torch.Tensor, q_frame0: int, n_q_frames: int,
                     shots: Sequence[int], out_dtype=torch.bfloat16,
                     softmax_scale: Optional[float] = None,
-                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    out: Optional[torch.Tensor] = None, n_workgroups: int = 0,
+                    split: bool = True) -> torch.Tensor:
     """fp4kv_attention_chunk: q_rot float32 or bf16 [n_q_frames*T][H][D],
-    already rotated by rope_rel."""
+    already rotated by rope_rel.  The work is split over n_workgroups
+    workgroups (0 = one per compute unit) using the cache's attention
+    workspace; split=False passes no workspace (one workgroup per 256-row
+    block)."""
     _require(q_rot, "q_rot", None, cache.device)
     if q_rot.dtype not in _DTYPES:
         raise ValueError("q_rot must be float32 or bfloat16")
@@ -170,18 +181,14 @@ def attention_chunk(cache: FP4KVCache, q_rot: torch.Tensor, q_frame0: int, n_q_f
         out = torch.empty(q_rot.shape, dtype=out_dtype, device=q_rot.device)
     _require(out, "out", out_dtype, cache.device)
     scale = 1.0 / math.sqrt(cache.D) if softmax_scale is None else softmax_scale
+    ws = cache.attn_workspace if split else None
     st = load().fp4kv_attention_chunk(
         ctypes.byref(cache.desc), q_rot.data_ptr(), _DTYPES[q_rot.dtype], out.data_ptr(),
         _DTYPES[out_dtype], q_frame0, n_q_frames, _i32_array(shots), cache.cos_sin.data_ptr(),
-        cache.n_pos, scale, _stream(cache.device))
+        cache.n_pos, scale, int(n_workgroups), _ptr(ws), 0 if ws is None else ws.numel(),
+        _stream(cache.device))
     check(st, "fp4kv_attention_chunk")
     return out
-
-
-def set_attention_workgroups(n: int) -> None:
-    """fp4kv_attention_set_workgroups: split the attention work over n
-    workgroups (capped at the number of compute units); 0 = default."""
-    check(load().fp4kv_attention_set_workgroups(int(n)), "fp4kv_attention_set_workgroups")
 
 
 def cache_positions(S: int, W: int, f0: int, n: int) -> int:

@@ -8,6 +8,8 @@
 #include "fp4kv.h"
 #include "internal.hpp"
 
+#include <algorithm>
+
 using namespace fp4kv;
 
 namespace {
@@ -188,7 +190,8 @@ int fp4kv_rope_rel(const void *x, int in_dtype, void *y, int out_dtype, int64_t 
 int fp4kv_attention_chunk(const fp4kv_cache *c, const void *q_rot, int q_dtype, void *o,
                           int out_dtype, int32_t q_frame0, int32_t n_q_frames,
                           const int32_t *q_shot, const float *cos_sin, int32_t n_pos,
-                          float softmax_scale, void *stream) {
+                          float softmax_scale, int32_t n_workgroups, void *workspace,
+                          size_t workspace_bytes, void *stream) {
   int st = check_shape(c);
   if (st) return st;
   if ((st = check_buffers(c))) return st;
@@ -232,13 +235,42 @@ int fp4kv_attention_chunk(const fp4kv_cache *c, const void *q_rot, int q_dtype, 
   p.Nq = (int)nq;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   for (int j = 0; j < n_q_frames; ++j) p.q_shot[j] = q_shot[j];
+
+  // Work split: equal ranges of the virtual key tiles (n_v per row block)
+  // over n_wg workgroups; without a workspace, one row block per workgroup.
+  const long long n_rb = (nq + kAttnRows - 1) / kAttnRows * c->n_heads;
+  const long long n_v = (long long)p.n_slots * ((p.Tc + 63) / 64);
+  long long n_wg = n_rb;
+  if (workspace) {
+    if (n_workgroups < 0 || n_workgroups > FP4KV_MAX_WORKGROUPS) return FP4KV_EINVAL;
+    if (!aligned16(workspace)) return FP4KV_EALIGN;
+    if (n_workgroups == 0) {
+      int dev = 0, cus = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return FP4KV_EDEVICE;
+      n_wg = std::min<long long>(std::min(cus, FP4KV_MAX_WORKGROUPS),
+                                 std::max<long long>(1, n_rb * n_v / 4));
+    } else {
+      n_wg = n_workgroups;
+    }
+    n_wg = std::min(n_wg, n_rb * n_v);   // no empty range
+    if (workspace_bytes < attn_workspace_bytes(c->head_dim, n_wg)) return FP4KV_ESHAPE;
+    uint8_t *ws = (uint8_t *)workspace;
+    p.ws_cnt = (int32_t *)ws;
+    p.ws_ml = (float2 *)(ws + kAttnCounterBytes);
+    p.ws_o = (float *)(ws + kAttnCounterBytes + (size_t)n_wg * 2 * kAttnRows * sizeof(float2));
+  }
+  if (n_wg > (1ll << 30)) return FP4KV_ESHAPE;
+  p.n_wg = (int)n_wg;
   return from_hip(launch_attention(p, c->head_dim, out_dtype == FP4KV_F32, (hipStream_t)stream));
 }
 
-int fp4kv_attention_set_workgroups(int32_t n) {
-  if (n < 0) return FP4KV_EINVAL;
-  g_attention_workgroups.store(n);
-  return FP4KV_OK;
+size_t fp4kv_attention_workspace_bytes(int32_t head_dim, int32_t n_workgroups) {
+  if ((head_dim != 64 && head_dim != 128) || n_workgroups < 1 ||
+      n_workgroups > FP4KV_MAX_WORKGROUPS)
+    return 0;
+  return attn_workspace_bytes(head_dim, n_workgroups);
 }
 
 }  // extern "C"

@@ -42,11 +42,6 @@
 #include "fp4kv_device.hpp"
 #include "internal.hpp"
 
-#include <algorithm>
-#include <map>
-#include <mutex>
-#include <utility>
-
 namespace fp4kv {
 namespace {
 
@@ -882,86 +877,21 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
   }
 }
 
-constexpr int kMinPiece = 4;   // fewest virtual tiles per workgroup range
-
-struct SplitWs {
-  float *o = nullptr;
-  float2 *ml = nullptr;
-  int *cnt = nullptr;
-};
-
-// Workspace of the split schedule, one per (device, stream) so that launches
-// on different streams never share it, sized for max_wg workgroups at head
-// dimension 128.  Allocated on first use (the counters are zeroed and the
-// device synchronized once) and kept until the process ends.
-hipError_t split_workspace(int dev, hipStream_t s, int max_wg, SplitWs &out) {
-  static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, SplitWs> cache;
-  std::lock_guard<std::mutex> lock(mu);
-  const auto it = cache.find({dev, s});
-  if (it != cache.end()) {
-    out = it->second;
-    return hipSuccess;
-  }
-  const size_t n_o = (size_t)2 * max_wg * kBM * 128, n_ml = (size_t)2 * max_wg * kBM;
-  const size_t bytes = n_o * sizeof(float) + n_ml * sizeof(float2) + (size_t)max_wg * sizeof(int);
-  void *buf = nullptr;
-  hipError_t e = hipMalloc(&buf, bytes);
-  if (e != hipSuccess) return e;
-  SplitWs ws;
-  ws.o = (float *)buf;
-  ws.ml = (float2 *)(ws.o + n_o);
-  ws.cnt = (int *)(ws.ml + n_ml);
-  e = hipMemset(ws.cnt, 0, (size_t)max_wg * sizeof(int));
-  if (e == hipSuccess) e = hipDeviceSynchronize();
-  if (e != hipSuccess) {
-    (void)hipFree(buf);
-    return e;
-  }
-  cache[{dev, s}] = ws;
-  out = ws;
-  return hipSuccess;
-}
-
 template <int D, bool OUT_F32>
-hipError_t launch_one(AttnParams &p, hipStream_t s) {
+hipError_t launch_one(const AttnParams &p, hipStream_t s) {
   constexpr size_t bytes = smem_bytes<D>();
   static const hipError_t attr = hipFuncSetAttribute(
       (const void *)attention_kernel<D, OUT_F32>, hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)bytes);
   if (attr != hipSuccess) return attr;
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  // One workgroup per CU (one fits a CU), each range at least kMinPiece
-  // virtual tiles long: a few row blocks are spread over all CUs, and a
-  // count that is not a multiple of the CUs is balanced instead of leaving a
-  // partial last round.
-  const long long n_rb = (long long)((p.Nq + kBM - 1) / kBM) * p.H;
-  const long long n_v = (long long)p.n_slots * ((p.Tc + kBN - 1) / kBN);
-  long long n_wg = std::min<long long>(cus, std::max<long long>(1, n_rb * n_v / kMinPiece));
-  const int forced = g_attention_workgroups.load();
-  if (forced > 0) n_wg = std::min(forced, cus);
-  n_wg = std::min(n_wg, n_rb * n_v);   // no empty range
-  p.n_wg = (int)n_wg;
-  if (n_rb % n_wg != 0) {   // some row blocks are shared between workgroups
-    SplitWs ws;
-    if ((e = split_workspace(dev, s, cus, ws)) != hipSuccess) return e;
-    p.ws_o = ws.o;
-    p.ws_ml = ws.ml;
-    p.ws_cnt = ws.cnt;
-  }
-  const dim3 grid((unsigned)((n_wg + kXcds - 1) / kXcds * kXcds));
+  const dim3 grid((unsigned)((p.n_wg + kXcds - 1) / kXcds * kXcds));
   hipLaunchKernelGGL((attention_kernel<D, OUT_F32>), grid, dim3(kThreads), bytes, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-std::atomic<int> g_attention_workgroups{0};
-
-hipError_t launch_attention(AttnParams &p, int head_dim, int out_f32, hipStream_t s) {
+hipError_t launch_attention(const AttnParams &p, int head_dim, int out_f32, hipStream_t s) {
   if (head_dim == 128) return out_f32 ? launch_one<128, true>(p, s) : launch_one<128, false>(p, s);
   return out_f32 ? launch_one<64, true>(p, s) : launch_one<64, false>(p, s);
 }

@@ -4,8 +4,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <atomic>
-
 #include "fp4kv.h"
 
 namespace fp4kv {
@@ -59,10 +57,15 @@ struct AttnParams {
 hipError_t launch_cache_reset(const fp4kv_cache &c, hipStream_t s);
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
 hipError_t launch_rope(const RopeParams &p, hipStream_t s);
-// Fills n_wg and the workspace pointers of p, then launches.
-hipError_t launch_attention(AttnParams &p, int head_dim, int out_f32, hipStream_t s);
+hipError_t launch_attention(const AttnParams &p, int head_dim, int out_f32, hipStream_t s);
 
-// Workgroups of the attention split schedule: 0 = one per compute unit.
-extern std::atomic<int> g_attention_workgroups;
+// Attention workspace: FP4KV_MAX_WORKGROUPS counters, then per workgroup two
+// partial (m, l) rows [2 n_wg][256] float2, then two partial outputs
+// [2 n_wg][256][D] float.
+constexpr size_t kAttnCounterBytes = FP4KV_MAX_WORKGROUPS * sizeof(int32_t);
+constexpr int kAttnRows = 256;
+inline size_t attn_workspace_bytes(int head_dim, long long n_wg) {
+  return kAttnCounterBytes + (size_t)n_wg * 2 * kAttnRows * (8 + 4 * (size_t)head_dim);
+}
 
 }  // namespace fp4kv

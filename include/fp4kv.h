@@ -62,6 +62,7 @@ extern "C" {
 /* Limits.  Frames per call and cache slots are passed to kernels by value. */
 #define FP4KV_MAX_FRAMES 64   /* frames per append or attention call      */
 #define FP4KV_MAX_SLOTS  64   /* sink + window frames (S + W)             */
+#define FP4KV_MAX_WORKGROUPS 4096 /* attention work split                  */
 
 /*
  * fp4kv_cache - descriptor of one layer's NVFP4 KV cache.
@@ -239,28 +240,35 @@ int fp4kv_rope_rel(const void *x, int in_dtype, void *y, int out_dtype, int64_t 
  * Rows with no visible key are written as zeros.
  *
  * Work split: the key tiles of all (256-row block, head) pairs are cut into
- * one contiguous range per workgroup (by default one workgroup per compute
- * unit).  A row block shared by two or more ranges is merged from partial
- * results (log-sum-exp combine).  That needs a workspace, which the library
- * allocates on the first such call on each (device, stream) pair: about
- * 68 MB on a 256-CU device (hipMalloc, then one device synchronization), kept
- * until the process ends.  Make that first call outside stream capture.
- * Calls on one stream are ordered; calls on different streams use different
- * workspaces.
+ * one contiguous range per workgroup.  A row block shared by two or more
+ * ranges is merged from partial results (log-sum-exp combine, in a fixed
+ * order, so repeated calls give identical bytes) kept in the workspace.
+ *   n_workgroups  0: one workgroup per compute unit of the current device
+ *                 (each range at least 4 key tiles); n > 0: n workgroups
+ *                 (at most FP4KV_MAX_WORKGROUPS).  With workspace == NULL
+ *                 the argument is ignored and every row block gets its own
+ *                 workgroup (no split, no workspace).
+ *   workspace     device, at least fp4kv_attention_workspace_bytes(D, n)
+ *                 bytes for the n workgroups used, 16-byte aligned, or NULL.
+ *                 It must be zero-filled once before its first use; every
+ *                 call leaves it ready for the next one.  Calls that overlap
+ *                 in time must use different workspaces.
+ * Errors: FP4KV_ESHAPE when the workspace is too small for the workgroups.
  */
 int fp4kv_attention_chunk(const fp4kv_cache *c, const void *q_rot, int q_dtype, void *o,
                           int out_dtype, int32_t q_frame0, int32_t n_q_frames,
                           const int32_t *q_shot, const float *cos_sin,
-                          int32_t n_pos, float softmax_scale, void *stream);
+                          int32_t n_pos, float softmax_scale, int32_t n_workgroups,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * fp4kv_attention_set_workgroups - number of workgroups the attention work is
- * split over, for tuning and tests: n > 0 uses min(n, compute units), 0
- * restores the default (one per compute unit, each with at least 4 key
- * tiles).  Process-wide; affects later fp4kv_attention_chunk calls.
- * Returns FP4KV_EINVAL for n < 0.
+ * Bytes of attention workspace for n_workgroups workgroups (1 ..
+ * FP4KV_MAX_WORKGROUPS) at head dimension head_dim (64 or 128): per
+ * workgroup two partial results of 256 rows (head_dim floats plus a (max,
+ * sum) pair each), plus FP4KV_MAX_WORKGROUPS counters.  0 for invalid
+ * arguments.  About 68 MB for 256 workgroups at head_dim 128.
  */
-int fp4kv_attention_set_workgroups(int32_t n);
+size_t fp4kv_attention_workspace_bytes(int32_t head_dim, int32_t n_workgroups);
 
 #ifdef __cplusplus
 }

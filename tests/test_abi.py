@@ -64,11 +64,15 @@ def test_strerror_and_version():
     assert lib.fp4kv_append_workspace_bytes() >= 64
 
 
-def test_attention_workgroup_knob():
+def test_attention_workspace_bytes():
     lib = _lib.load()
-    assert lib.fp4kv_attention_set_workgroups(-1) == _lib.FP4KV_EINVAL
-    assert lib.fp4kv_attention_set_workgroups(7) == 0
-    assert lib.fp4kv_attention_set_workgroups(0) == 0
+    counters = 4 * _lib.FP4KV_MAX_WORKGROUPS
+    # per workgroup: 2 partial results x 256 rows x (D floats + (m, l))
+    assert lib.fp4kv_attention_workspace_bytes(128, 1) == counters + 2 * 256 * (4 * 128 + 8)
+    assert lib.fp4kv_attention_workspace_bytes(64, 256) == counters + 256 * 2 * 256 * (4 * 64 + 8)
+    assert lib.fp4kv_attention_workspace_bytes(128, 256) < 70_000_000
+    for d, n in ((96, 4), (128, 0), (128, -1), (64, _lib.FP4KV_MAX_WORKGROUPS + 1)):
+        assert lib.fp4kv_attention_workspace_bytes(d, n) == 0
 
 
 def test_cache_nbytes():
@@ -159,10 +163,18 @@ def test_attention_validation_before_launch():
     c = _desc()
     A, B = 0x100000, 0x200000
     shots = (ctypes.c_int32 * 4)(0, 0, 0, 0)
+    W = 0x4000000
+    ws_bytes = lib.fp4kv_attention_workspace_bytes(128, 4)
     call = lambda **kw: lib.fp4kv_attention_chunk(
         ctypes.byref(kw.get("c", c)), kw.get("q", A), kw.get("qdt", 0), kw.get("o", B),
         kw.get("dt", 1), kw.get("f0", 0), kw.get("n", 3), kw.get("shots", shots), kw.get("cs", A),
-        kw.get("npos", 15), kw.get("scale", 0.088), None)
+        kw.get("npos", 15), kw.get("scale", 0.088), kw.get("nwg", 4), kw.get("ws", W),
+        kw.get("wsb", ws_bytes), None)
+    assert call(nwg=-1) == -1
+    assert call(nwg=_lib.FP4KV_MAX_WORKGROUPS + 1) == -1
+    assert call(wsb=ws_bytes - 1) == -2          # too small for 4 workgroups
+    assert call(nwg=5) == -2
+    assert call(ws=W + 8) == -3
     assert call(q=None) == -1
     assert call(o=A) == -1             # aliasing
     assert call(n=0) == -1

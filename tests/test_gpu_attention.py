@@ -19,19 +19,22 @@ pytestmark = pytest.mark.gpu
 MAX_ABS, MEAN_ABS = 1e-2, 1e-3
 
 
-def _gpu_step(api, gc, w, c, q, qb, k, kb, v, vb, out_dtype=torch.float32, append=True):
+def _gpu_step(api, gc, w, c, q, qb, k, kb, v, vb, out_dtype=torch.float32, append=True,
+              n_wg=0, split=True):
     f0, n = w.chunk_frames(c)
     shots = shots_of(w, f0, n)
     if append:
         api.quantize_append(gc, device_tensor(k, kb), device_tensor(v, vb), f0, n, shots)
     pos0 = api.cache_positions(w.S, w.W, f0, n)
     qr = api.rope_rel(device_tensor(q, qb), pos0, w.T, gc.cos_sin, rot_dim=gc.rot_dim)
-    o = api.attention_chunk(gc, qr, f0, n, shots, out_dtype=out_dtype)
+    o = api.attention_chunk(gc, qr, f0, n, shots, out_dtype=out_dtype, n_workgroups=n_wg,
+                            split=split)
     torch.cuda.synchronize()
     return o.float().cpu().numpy()
 
 
-def _run_stream(w, steps, rows=None, heads=None, check_every=True, rot_dim=None):
+def _run_stream(w, steps, rows=None, heads=None, check_every=True, rot_dim=None, n_wg=0,
+                split=True):
     from fp4_kv_cache_fp4kv_amd import api
     gc, oc = gpu_cache(w, rot_dim), OracleCache.for_workload(w, rot_dim)
     results = []
@@ -47,7 +50,7 @@ def _run_stream(w, steps, rows=None, heads=None, check_every=True, rot_dim=None)
         if f0 < w.S or f0 + n > f1_next - w.W:
             oc.append(k, v, f0, n, shots)
         say(f"attention {w.name} step {c} frames {f0}..{f0 + n - 1}")
-        got = _gpu_step(api, gc, w, c, q, qb, k, kb, v, vb)
+        got = _gpu_step(api, gc, w, c, q, qb, k, kb, v, vb, n_wg=n_wg, split=split)
         if c not in steps:
             continue
         assert not compare_cache(gc, oc), (w.name, c)
@@ -136,55 +139,51 @@ def test_attention_empty_cache_gives_zeros():
     assert torch.count_nonzero(o).item() == 0
 
 
-@pytest.fixture
-def workgroups():
-    from fp4_kv_cache_fp4kv_amd import api
-    yield api.set_attention_workgroups
-    api.set_attention_workgroups(0)
-
-
 # 4 row blocks of 300 rows x 2 heads, 14 key tiles each at a full window
 # (7 slots x 2 tiles, the second ragged): 1 workgroup takes every row block
 # whole; 3, 5 and 13 workgroups cut row blocks into 2 to 4 merged pieces.
 @pytest.mark.parametrize("n_wg", [1, 3, 5, 13])
-def test_attention_split_schedules(n_wg, workgroups):
-    workgroups(n_wg)
+def test_attention_split_schedules(n_wg):
     w = wl.Workload("split", H=2, D=128, T=100, C=3, S=1, W=6, n_frames=15, seed=24,
                     outlier_p=0.01, outlier_scale=20.0)
-    _run_stream(w, [1, 4])
+    _run_stream(w, [1, 4], n_wg=n_wg)
+
+
+def test_attention_without_workspace():
+    """No workspace: one workgroup per row block, no split."""
+    w = wl.Workload("split", H=2, D=128, T=100, C=3, S=1, W=6, n_frames=15, seed=24,
+                    outlier_p=0.01, outlier_scale=20.0)
+    _run_stream(w, [1, 4], split=False)
 
 
 @pytest.mark.parametrize("n_wg", [2, 7])
-def test_attention_split_multishot_d64(n_wg, workgroups):
-    workgroups(n_wg)
+def test_attention_split_multishot_d64(n_wg):
     w = wl.Workload("tiny_mix", H=3, D=64, T=24, C=3, S=2, W=6, n_frames=20, seed=21,
                     dtype="bf16", token_stride=2, shot_len=5)
-    _run_stream(w, list(range(w.n_chunks)))
+    _run_stream(w, list(range(w.n_chunks)), n_wg=n_wg)
 
 
-def test_attention_split_is_deterministic(workgroups):
+def test_attention_split_is_deterministic():
     """Merged pieces are combined in a fixed order: repeated calls give the
     same bytes, whichever workgroup finishes a row block last."""
     from fp4_kv_cache_fp4kv_amd import api
-    workgroups(13)
     w = wl.Workload("split", H=2, D=128, T=100, C=3, S=1, W=6, n_frames=15, seed=24,
                     outlier_p=0.01, outlier_scale=20.0)
     gc = gpu_cache(w)
     for c in range(3):
         f0, n = w.chunk_frames(c)
         (q, qb), (k, kb), (v, vb) = step_inputs(w, c)
-        outs = [_gpu_step(api, gc, w, c, q, qb, k, kb, v, vb, append=(i == 0))
+        outs = [_gpu_step(api, gc, w, c, q, qb, k, kb, v, vb, append=(i == 0), n_wg=13)
                 for i in range(3)]
         assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
 
-def test_attention_split_empty_cache_gives_zeros(workgroups):
+def test_attention_split_empty_cache_gives_zeros():
     from fp4_kv_cache_fp4kv_amd import api
-    workgroups(3)
     w = wl.TINY
     gc = gpu_cache(w)
     q = torch.randn(2 * w.T, w.H, w.D, device="cuda:0").bfloat16()
-    o = api.attention_chunk(gc, q, 0, 2, [0, 0], out_dtype=torch.float32)
+    o = api.attention_chunk(gc, q, 0, 2, [0, 0], out_dtype=torch.float32, n_workgroups=3)
     torch.cuda.synchronize()
     assert torch.count_nonzero(o).item() == 0
 
@@ -205,6 +204,15 @@ def test_attention_full_size_sampled(name):
     steady = (w.S + w.W) // w.C          # first step with a full window
     steps = [0, steady - 1] if name == "l13b" else [0, steady, steady + 3]
     _run_stream(w, steps, rows=_sample_rows(w), heads=[0, w.H // 2, w.H - 1])
+
+
+def test_attention_full_size_without_workspace():
+    """5B-like layer with one workgroup per row block (264 of them: a
+    second round on 256 CUs)."""
+    w = wl.L5B
+    steady = (w.S + w.W) // w.C
+    _run_stream(w, [steady], rows=_sample_rows(w, n_rows=24, seed=3), heads=[1, w.H - 1],
+                split=False)
 
 
 def test_attention_multishot_full_size_sampled():
