@@ -62,8 +62,9 @@ class Workload:
         return 0 if self.shot_len is None else f // self.shot_len
 
 
-# The five workloads (listed small to large).  "tiny" is the oracle-sized
-# case; the others are shaped like one attention layer of the generators.
+# The five configurations (listed small to large), then one GPU's head
+# share.  "tiny" is the oracle-sized case; the others are shaped like one
+# attention layer of the generators.
 TINY = Workload("tiny", H=1, D=64, T=16, C=2, S=1, W=4, n_frames=12, seed=0,
                 dtype="f32")
 L13B = Workload("l13b", H=12, D=128, T=1560, C=3, S=3, W=12, n_frames=15,
@@ -73,8 +74,12 @@ L5B_SHOTS = Workload("l5b_shots", H=24, D=128, T=880, C=3, S=3, W=12,
                      n_frames=80, seed=4, shot_len=20)
 LONG = Workload("long", H=24, D=128, T=880, C=3, S=3, W=21, n_frames=720,
                 seed=5, token_stride=2)
+# One GPU's share of the 5B-like layer when 8 GPUs split its 24 heads: 3
+# heads, 33 row blocks of 256 query rows (the case the split attention
+# schedule exists for).
+L5B_SHARE = Workload("l5b_share", H=3, D=128, T=880, C=3, S=3, W=12, n_frames=90, seed=6)
 
-WORKLOADS = {w.name: w for w in (TINY, L13B, L5B, L5B_SHOTS, LONG)}
+WORKLOADS = {w.name: w for w in (TINY, L13B, L5B, L5B_SHOTS, LONG, L5B_SHARE)}
 
 
 def bf16_round(x: np.ndarray):

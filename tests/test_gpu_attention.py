@@ -215,6 +215,15 @@ def test_attention_full_size_without_workspace():
                 split=False)
 
 
+@pytest.mark.parametrize("split", [True, False])
+def test_attention_head_share_sampled(split):
+    """3 heads of the 5B-like layer (one GPU's share of 8): 33 row blocks,
+    split over every CU or one workgroup each."""
+    w = wl.L5B_SHARE
+    steady = (w.S + w.W) // w.C
+    _run_stream(w, [steady, steady + 2], rows=_sample_rows(w, seed=4), split=split)
+
+
 def test_attention_multishot_full_size_sampled():
     w = wl.L5B_SHOTS
     # step 6 holds frames 18..20 (the shot boundary cuts the chunk); step 26 is partial
