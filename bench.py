@@ -187,8 +187,10 @@ def main():
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
-    attn_ms = sum(a.elapsed_time(b) for a, b in zip(ev["a0"], ev["a1"])) / args.steps
+    attn_each = sorted(a.elapsed_time(b) for a, b in zip(ev["a0"], ev["a1"]))
+    attn_ms = sum(attn_each) / args.steps
     codec_ms = sum(a.elapsed_time(b) for a, b in zip(ev["c0"], ev["c1"])) / args.steps
+    pct = lambda v, q: v[min(len(v) - 1, int(q * len(v)))]
 
     Nq, Nk = w.C * w.T, (w.S + w.W) * w.Tc
     flops = 4.0 * w.H * Nq * Nk * w.D
@@ -223,6 +225,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_desc(w), "query_rows": Nq, "keys": Nk,
                    "frames_per_step": w.C, "attention_ms": round(attn_ms, 4),
+                   "attention_ms_p10_p50_p90": [round(pct(attn_each, q), 4)
+                                                for q in (0.1, 0.5, 0.9)],
                    "append_ms": round(codec_ms, 4)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4),
