@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="l13b")
+    ap.add_argument("--kv", default="nvfp4", choices=("nvfp4", "bf16"),
+                    help="cache format: NVFP4 (the path) or the bf16 baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters")
@@ -133,7 +135,8 @@ def main():
 
     w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    gc = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride, device="cuda:0")
+    gc = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride, device="cuda:0",
+                        kv_format=args.kv)
 
     def dev_t(vals, bits):
         if bits is not None:
@@ -197,7 +200,7 @@ def main():
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     es = 2 if w.dtype == "bf16" else 4
     kept = 2 * w.C * w.Tc * w.H * w.D
-    codec_bytes = kept * es + kept * (0.5 + 1.0 / 16.0)
+    codec_bytes = kept * es + kept * (2.0 if args.kv == "bf16" else 0.5 + 1.0 / 16.0)
     codec_gbs = codec_bytes / (codec_ms * 1e-3) / 1e9
 
     # HBM bytes per attention launch from rocprofv3 counters, valid only for
@@ -205,7 +208,8 @@ def main():
     traffic = None
     try:
         tj = json.load(open(args.traffic_json))
-        if tj.get("workload") == w.name and tj.get("source_hash") == attention_source_hash():
+        if (tj.get("workload") == w.name and tj.get("source_hash") == attention_source_hash()
+                and args.kv == "nvfp4"):
             traffic = tj.get("attention_bytes_per_launch")
     except (OSError, ValueError):
         pass
@@ -223,7 +227,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": workload_desc(w), "query_rows": Nq, "keys": Nk,
+        "config": {"workload": workload_desc(w), "kv_format": args.kv, "query_rows": Nq,
+                   "keys": Nk,
                    "frames_per_step": w.C, "attention_ms": round(attn_ms, 4),
                    "attention_ms_p10_p50_p90": [round(pct(attn_each, q), 4)
                                                 for q in (0.1, 0.5, 0.9)],
@@ -235,7 +240,7 @@ def main():
                            "unit": "GB/s", "frac": round(codec_gbs / HBM_PEAK_GBS, 4),
                            "bytes": int(codec_bytes)},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.kv == "nvfp4":
         res["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(res), flush=True)
 

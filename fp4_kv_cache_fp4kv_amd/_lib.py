@@ -20,6 +20,7 @@ FP4KV_EDEVICE = -5
 FP4KV_F32 = 0
 FP4KV_BF16 = 1
 FP4KV_FORMAT_NVFP4_V1 = 0x3146564E
+FP4KV_FORMAT_BF16_V1 = 0x36314642
 FP4KV_MAX_FRAMES = 64
 FP4KV_MAX_WORKGROUPS = 4096
 FP4KV_MAX_SLOTS = 64

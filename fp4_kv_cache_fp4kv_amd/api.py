@@ -43,23 +43,28 @@ def _require(t: torch.Tensor, name: str, dtype=None, device=None):
 
 
 class FP4KVCache:
-    """Caller-owned buffers of one layer's NVFP4 KV cache plus its descriptor.
+    """Caller-owned buffers of one layer's KV cache plus its descriptor.
 
-    Layout (see include/fp4kv.h): codes uint8 [H][S+W][Tc][D/2], scales
-    uint8 [H][S+W][Tc][D/16], tensor scales float32 [S+W], slot metadata
-    int32 [S+W].
+    kv_format "nvfp4" (layout in include/fp4kv.h: codes uint8
+    [H][S+W][Tc][D/2], scales uint8 [H][S+W][Tc][D/16], tensor scales float32
+    [S+W], slot metadata int32 [S+W]) or "bf16", the unquantized baseline
+    (keys bf16 [H][S+W][Tc][D], values bf16 [H][S+W][D][Tv], no scales).
     """
 
     def __init__(self, H: int, D: int, T: int, C: int, S: int, W: int,
                  token_stride: int = 1, rot_dim: Optional[int] = None,
-                 device: str = "cuda:0"):
+                 device: str = "cuda:0", kv_format: str = "nvfp4"):
         lib = load()
+        if kv_format not in ("nvfp4", "bf16"):
+            raise ValueError("kv_format must be 'nvfp4' or 'bf16'")
+        self.kv_format = kv_format
         self.device = torch.device(device)
         self.H, self.D, self.T, self.C, self.S, self.W = H, D, T, C, S, W
         self.token_stride = token_stride
         self.Tc = T // token_stride
         self.rot_dim = D if rot_dim is None else rot_dim
-        self.desc = CacheDesc(format_tag=_lib.FP4KV_FORMAT_NVFP4_V1, n_heads=H, head_dim=D,
+        tag = _lib.FP4KV_FORMAT_NVFP4_V1 if kv_format == "nvfp4" else _lib.FP4KV_FORMAT_BF16_V1
+        self.desc = CacheDesc(format_tag=tag, n_heads=H, head_dim=D,
                               tokens_per_frame=T, token_stride=token_stride, chunk_frames=C,
                               sink_frames=S, window_frames=W, rot_dim=self.rot_dim)
         sizes = (ctypes.c_size_t * 6)()
@@ -77,7 +82,8 @@ class FP4KVCache:
         self.slot_shot = torch.zeros(n, dtype=torch.int32, device=dev)
         for name in ("k_codes", "v_codes", "k_scales", "v_scales", "k_tscale", "v_tscale",
                      "slot_frame", "slot_shot"):
-            setattr(self.desc, name, getattr(self, name).data_ptr())
+            t = getattr(self, name)
+            setattr(self.desc, name, t.data_ptr() if t.numel() else 0)
         self.workspace = torch.zeros(lib.fp4kv_append_workspace_bytes(), dtype=torch.uint8,
                                      device=dev)
         # attention workspace for up to one workgroup per compute unit,
@@ -94,6 +100,11 @@ class FP4KVCache:
     # views in the documented layout (for tests and inspection)
     def views(self):
         H, n, Tc, Tv, D = self.H, self.S + self.W, self.Tc, self.Tv, self.D
+        if self.kv_format == "bf16":
+            return dict(k_codes=self.k_codes.view(torch.int16).view(H, n, Tc, D),
+                        v_codes=self.v_codes.view(torch.int16).view(H, n, D, Tv),
+                        k_tscale=self.k_tscale, v_tscale=self.v_tscale,
+                        slot_frame=self.slot_frame, slot_shot=self.slot_shot)
         return dict(k_codes=self.k_codes.view(H, n, Tc, D // 2),
                     v_codes=self.v_codes.view(H, n, D, Tv // 2),
                     k_scales=self.k_scales.view(H, n, Tc, D // 16),

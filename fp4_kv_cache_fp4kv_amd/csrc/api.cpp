@@ -27,7 +27,8 @@ int padded_tokens(const fp4kv_cache *c) {
 // Shape checks of a cache descriptor (no pointer reads).
 int check_shape(const fp4kv_cache *c) {
   if (!c) return FP4KV_EINVAL;
-  if (c->format_tag != FP4KV_FORMAT_NVFP4_V1) return FP4KV_EFORMAT;
+  if (c->format_tag != FP4KV_FORMAT_NVFP4_V1 && c->format_tag != FP4KV_FORMAT_BF16_V1)
+    return FP4KV_EFORMAT;
   if (c->n_heads < 1 || c->tokens_per_frame < 1 || c->chunk_frames < 1 || c->sink_frames < 0)
     return FP4KV_EINVAL;
   if (c->head_dim != 64 && c->head_dim != 128) return FP4KV_ESHAPE;
@@ -42,12 +43,15 @@ int check_shape(const fp4kv_cache *c) {
   return FP4KV_OK;
 }
 
+bool is_bf16(const fp4kv_cache *c) { return c->format_tag == FP4KV_FORMAT_BF16_V1; }
+
 int check_buffers(const fp4kv_cache *c) {
-  const void *ptrs[] = {c->k_codes, c->v_codes, c->k_scales, c->v_scales,
-                        c->k_tscale, c->v_tscale, c->slot_frame, c->slot_shot};
-  for (const void *p : ptrs) {
-    if (!p) return FP4KV_EINVAL;
-    if (!aligned16(p)) return FP4KV_EALIGN;
+  const void *ptrs[] = {c->k_codes, c->v_codes, c->k_tscale, c->v_tscale,
+                        c->slot_frame, c->slot_shot, c->k_scales, c->v_scales};
+  const int n = is_bf16(c) ? 6 : 8;   // the bf16 format has no scale buffers
+  for (int i = 0; i < n; ++i) {
+    if (!ptrs[i]) return FP4KV_EINVAL;
+    if (!aligned16(ptrs[i])) return FP4KV_EALIGN;
   }
   return FP4KV_OK;
 }
@@ -80,10 +84,16 @@ int fp4kv_cache_nbytes(const fp4kv_cache *c, size_t out[6]) {
   const size_t tc = (size_t)(c->tokens_per_frame / c->token_stride);
   const size_t tv = (size_t)padded_tokens(c);
   const size_t hs = (size_t)c->n_heads * slots, d = (size_t)c->head_dim;
-  out[0] = hs * tc * (d / 2);
-  out[1] = hs * d * (tv / 2);
-  out[2] = hs * tc * (d / 16);
-  out[3] = hs * (d / 16) * tv;
+  if (is_bf16(c)) {
+    out[0] = hs * tc * d * 2;
+    out[1] = hs * d * tv * 2;
+    out[2] = out[3] = 0;
+  } else {
+    out[0] = hs * tc * (d / 2);
+    out[1] = hs * d * (tv / 2);
+    out[2] = hs * tc * (d / 16);
+    out[3] = hs * (d / 16) * tv;
+  }
   out[4] = slots * sizeof(float);
   out[5] = slots * sizeof(int32_t);
   return FP4KV_OK;
@@ -140,6 +150,7 @@ int fp4kv_quantize_append(const fp4kv_cache *c, const void *k, const void *v, in
   p.frame0 = frame0;
   p.n_frames = n_frames;
   p.in_bf16 = in_dtype == FP4KV_BF16;
+  p.bf16_cache = is_bf16(c);
   for (int j = 0; j < n_frames; ++j) p.shot[j] = frame_shot[j];
   return from_hip(launch_append(p, (hipStream_t)stream));
 }
@@ -211,6 +222,7 @@ int fp4kv_attention_chunk(const fp4kv_cache *c, const void *q_rot, int q_dtype, 
   memset(&p, 0, sizeof(p));
   p.q = q_rot;
   p.q_f32 = q_dtype == FP4KV_F32;
+  p.bf16_cache = is_bf16(c);
   p.o = o;
   p.k_codes = c->k_codes;
   p.v_codes = c->v_codes;

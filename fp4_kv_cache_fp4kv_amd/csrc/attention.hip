@@ -148,23 +148,46 @@ struct RawV {
 // outside the K range and read as zero, value tokens past Tv are sent out of
 // range.  No branch, so the loads stay in flight until the codes are
 // dequantized two phases later.  lt is the thread's index in its group.
-template <bool K>
+// bf16 baseline format: the same elements as bf16 (two 16-byte words per
+// 16 elements).
+struct RawKB {
+  uint4 kc[4];     // 32 key elements
+};
+struct RawVB {
+  uint4 v[4];      // 16 tokens of two value dimensions: v[2 r], v[2 r + 1] = dimension r
+};
+template <bool K, bool BF16KV>
 struct RawOf {
   using type = RawV;
 };
 template <>
-struct RawOf<true> {
+struct RawOf<true, false> {
   using type = RawK;
+};
+template <>
+struct RawOf<false, true> {
+  using type = RawVB;
+};
+template <>
+struct RawOf<true, true> {
+  using type = RawKB;
 };
 
 // Buffer resources over one (head, slot) range of the four cache arrays.
 struct SlotRes {
   __amdgpu_buffer_rsrc_t kc, ks, vc, vs;
 };
-template <int D>
+template <int D, bool BF16KV>
 __device__ __forceinline__ SlotRes slot_resources(const AttnParams &p, int head, int slot) {
   const long long hs = (long long)head * p.n_slots + slot;
   SlotRes r;
+  if constexpr (BF16KV) {
+    r.kc = rsrc(p.k_codes + hs * p.Tc * D * 2, p.Tc * D * 2);
+    r.vc = rsrc(p.v_codes + hs * D * p.Tv * 2, D * p.Tv * 2);
+    r.ks = r.kc;   // no scales
+    r.vs = r.vc;
+    return r;
+  }
   r.kc = rsrc(p.k_codes + hs * p.Tc * (D / 2), p.Tc * (D / 2));
   r.ks = rsrc(p.k_scales + hs * p.Tc * (D / 16), p.Tc * (D / 16));
   r.vc = rsrc(p.v_codes + hs * D * (p.Tv / 2), D * (p.Tv / 2));
@@ -198,6 +221,42 @@ __device__ __forceinline__ void load_v(const SlotRes &sr, int Tv, int k0, int lt
     r.vc[1] = make_uint2(c1[0], c1[1]);
     r.vs = make_uint4(vs[0], vs[1], vs[2], vs[3]);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void load_k(const SlotRes &sr, int k0, int lt, RawKB &r) {
+  constexpr int KU = D / 32;
+  if (lt < kBN * KU) {
+    const uint32_t off = (k0 + lt / KU) * (D * 2) + 64 * (lt % KU);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(sr.kc, off + 16 * i, 0, 0);
+      r.kc[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+template <int D>
+__device__ __forceinline__ void load_v(const SlotRes &sr, int Tv, int k0, int lt, RawVB &r) {
+  if (lt < 2 * D) {
+    const int rp = lt >> 2, kg = lt & 3;
+    const int tok = k0 + 16 * kg;
+    const bool ok = tok < Tv;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const uint32_t o = ok ? (uint32_t)(((2 * rp + rr) * Tv + tok) * 2) : kOutOfRange;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b128(sr.vc, o + 16 * i, 0, 0);
+        r.v[2 * rr + i] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  }
+}
+
+// Two bf16 values (a 32-bit word) -> f16x2 bits; exact within the f16 range.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const f16x2 h = {(_Float16)__uint_as_float(w << 16), (_Float16)__uint_as_float(w & 0xFFFF0000u)};
+  return bits(h);
 }
 
 // K rows past the end of the frame read as zero codes (their scores are
@@ -251,6 +310,34 @@ __device__ __forceinline__ void dequant_v(const RawV &r, int lt, uint16_t (*vt)[
       uint4 *dst = (uint4 *)&vt[2 * rp + rr][16 * kg];
       dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
       dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+  }
+}
+template <int D>
+__device__ __forceinline__ void dequant_k(const RawKB &r, int lt, uint16_t (*kt)[D + kPad]) {
+  constexpr int KU = D / 32;
+  if (lt < kBN * KU) {
+    const int key = lt / KU, qd = lt % KU;
+    uint4 *dst = (uint4 *)&kt[krow_phys(key)][32 * qd];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dst[i] = make_uint4(bf16x2_to_f16x2(r.kc[i].x), bf16x2_to_f16x2(r.kc[i].y),
+                          bf16x2_to_f16x2(r.kc[i].z), bf16x2_to_f16x2(r.kc[i].w));
+  }
+}
+template <int D>
+__device__ __forceinline__ void dequant_v(const RawVB &r, int lt, uint16_t (*vt)[kBN + kPad]) {
+  if (lt < 2 * D) {
+    const int rp = lt >> 2, kg = lt & 3;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      uint4 *dst = (uint4 *)&vt[2 * rp + rr][16 * kg];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint4 w = r.v[2 * rr + i];
+        dst[i] = make_uint4(bf16x2_to_f16x2(w.x), bf16x2_to_f16x2(w.y), bf16x2_to_f16x2(w.z),
+                            bf16x2_to_f16x2(w.w));
+      }
     }
   }
 }
@@ -459,7 +546,7 @@ __device__ __forceinline__ int walk_index(unsigned long long visible, int x, int
 // after an empty opening phase.  K(t) is written in phase 2t-1 and read in
 // phases 2t and 2t+1 (2 buffers); V(t) is written in phase 2t-2 and read in
 // phases 2t+2 and 2t+3 (3 buffers).
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, bool BF16KV>
 __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
   constexpr int KS = D / 16;   // k-steps of S^T over d
   constexpr int DB = D / 32;   // 32-row blocks of O^T
@@ -662,9 +749,9 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
       auto run_group = [&](auto gtag, auto ltag) __attribute__((always_inline)) {
         constexpr bool G = decltype(gtag)::value;
         constexpr bool L = decltype(ltag)::value;
-        typename RawOf<G>::type raw;
+        typename RawOf<G, BF16KV>::type raw;
         Cursor cd = {fa, ta, 0};
-        SlotRes res = slot_resources<D>(p, head, sm.fl_slot[fa]);   // frame of cd
+        SlotRes res = slot_resources<D, BF16KV>(p, head, sm.fl_slot[fa]);   // frame of cd
         auto load_half = [&]() __attribute__((always_inline)) {
           if constexpr (G) load_k<D>(res, cd.tt * kBN, lt, raw);
           else load_v<D>(res, p.Tv, cd.tt * kBN, lt, raw);
@@ -677,7 +764,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
           else dequant_v<D>(raw, lt, sm.vt[cd.i % kVBufs]);
           Cursor nx = advance(cd);
           nx.i = cd.i + 1;
-          if (nx.fi != cd.fi) res = slot_resources<D>(p, head, sm.fl_slot[nx.fi]);
+          if (nx.fi != cd.fi) res = slot_resources<D, BF16KV>(p, head, sm.fl_slot[nx.fi]);
           cd = nx;
           load_half();
         };
@@ -881,23 +968,30 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
   }
 }
 
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, bool BF16KV>
 hipError_t launch_one(const AttnParams &p, hipStream_t s) {
   constexpr size_t bytes = smem_bytes<D>();
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void *)attention_kernel<D, OUT_F32>, hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)bytes);
+      (const void *)attention_kernel<D, OUT_F32, BF16KV>,
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (attr != hipSuccess) return attr;
   const dim3 grid((unsigned)((p.n_wg + kXcds - 1) / kXcds * kXcds));
-  hipLaunchKernelGGL((attention_kernel<D, OUT_F32>), grid, dim3(kThreads), bytes, s, p);
+  hipLaunchKernelGGL((attention_kernel<D, OUT_F32, BF16KV>), grid, dim3(kThreads), bytes, s, p);
   return hipGetLastError();
+}
+
+template <bool BF16KV>
+hipError_t launch_kv(const AttnParams &p, int head_dim, int out_f32, hipStream_t s) {
+  if (head_dim == 128)
+    return out_f32 ? launch_one<128, true, BF16KV>(p, s) : launch_one<128, false, BF16KV>(p, s);
+  return out_f32 ? launch_one<64, true, BF16KV>(p, s) : launch_one<64, false, BF16KV>(p, s);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnParams &p, int head_dim, int out_f32, hipStream_t s) {
-  if (head_dim == 128) return out_f32 ? launch_one<128, true>(p, s) : launch_one<128, false>(p, s);
-  return out_f32 ? launch_one<64, true>(p, s) : launch_one<64, false>(p, s);
+  return p.bf16_cache ? launch_kv<true>(p, head_dim, out_f32, s)
+                      : launch_kv<false>(p, head_dim, out_f32, s);
 }
 
 }  // namespace fp4kv

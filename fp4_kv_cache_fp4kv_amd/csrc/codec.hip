@@ -2,11 +2,13 @@
 // of sink + window slots ("in-place quantized KV-cache updates",
 // hysenlabs.com, "NVFP4, sequence parallel and the async decode path").
 //
-// Two kernels per call, on the caller's stream:
+// NVFP4 caches take two kernels per call, on the caller's stream:
 //   amax_kernel    grid (kAmaxBlocks, 2): partial max |x| over the kept
 //                  tokens of K (y = 0) and V (y = 1), one per workgroup.
 //   encode_kernel  NVFP4 encode of both tensors straight into their cache
 //                  slots (layouts in include/fp4kv.h), plus the slot metadata.
+// The bf16 baseline format takes one kernel (store_bf16_kernel): a copy into
+// the same ring layout.
 #include "fp4kv_device.hpp"
 #include "internal.hpp"
 
@@ -252,6 +254,88 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(AppendParams p) {
   *(uint2 *)(p.scales[1] + srow * p.Tv + 8 * grp) = make_uint2(sc_lo, sc_hi);
 }
 
+// ---- bf16 baseline format: the append stores bf16, no quantization ----
+
+// float32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t bf16_rne(uint32_t u) {
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// 8 consecutive inputs as 4 words of packed bf16 pairs.
+__device__ __forceinline__ uint4 load8_bf16(const AppendParams &p, int y, long long src) {
+  if (p.in_bf16) return *(const uint4 *)((const uint16_t *)p.x[y] + src);
+  const uint4 a = *(const uint4 *)((const float *)p.x[y] + src);
+  const uint4 b = *(const uint4 *)((const float *)p.x[y] + src + 4);
+  return make_uint4(bf16_rne(a.x) | (bf16_rne(a.y) << 16), bf16_rne(a.z) | (bf16_rne(a.w) << 16),
+                    bf16_rne(b.x) | (bf16_rne(b.y) << 16), bf16_rne(b.z) | (bf16_rne(b.w) << 16));
+}
+
+// Workgroups [0, p.v_blocks) store values: one thread per (head, frame,
+// 8-token group, 8 dimensions) transposes an 8 x 8 tile into 8 dimension
+// rows of 16 bytes (padding tokens as zeros).  The others store keys: one
+// thread per (token, head, 8 dimensions) copies 16 bytes.
+__global__ __launch_bounds__(kThreads) void store_bf16_kernel(AppendParams p) {
+  const int n8 = p.D >> 3;
+  if ((int)blockIdx.x >= p.v_blocks) {
+    const uint32_t units = (uint32_t)(p.n_frames * p.Tc * p.H * n8);
+    const uint32_t u = (blockIdx.x - p.v_blocks) * kThreads + threadIdx.x;
+    if ((int)blockIdx.x == p.v_blocks && threadIdx.x < p.n_frames) {
+      const int j = threadIdx.x, f = p.frame0 + j, sl = slot_of(p, f);
+      p.tscale[0][sl] = 1.0f;
+      p.tscale[1][sl] = 1.0f;
+      p.slot_frame[sl] = f;
+      p.slot_shot[sl] = p.shot[j];
+    }
+    if (u >= units) return;
+    const int c8 = (int)(u % n8);
+    uint32_t rest = u / n8;
+    const int h = (int)(rest % p.H);
+    rest /= p.H;
+    const int tc = (int)(rest % p.Tc);
+    const int j = (int)(rest / p.Tc);
+    const long long tok = (long long)j * p.T + (long long)tc * p.stride;
+    const uint4 v = load8_bf16(p, 0, (tok * p.H + h) * p.D + 8 * c8);
+    const int slot = slot_of(p, p.frame0 + j);
+    const long long row = ((long long)h * p.n_slots + slot) * p.Tc + tc;
+    *(uint4 *)(p.codes[0] + (row * p.D + 8 * c8) * 2) = v;
+    return;
+  }
+  const int g8s = p.Tv >> 3;
+  const uint32_t units = (uint32_t)(p.H * p.n_frames * n8 * g8s);
+  const uint32_t u = blockIdx.x * kThreads + threadIdx.x;
+  if (u >= units) return;
+  const int g8 = (int)(u % g8s);
+  uint32_t rest = u / g8s;
+  const int c8 = (int)(rest % n8);
+  rest /= n8;
+  const int j = (int)(rest % p.n_frames);
+  const int h = (int)(rest / p.n_frames);
+  uint32_t e[8][4];   // e[token][word]: dims 8*c8 .. +7 of 8 tokens
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int tc = 8 * g8 + i;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (tc < p.Tc) {
+      const long long tok = (long long)j * p.T + (long long)tc * p.stride;
+      v = load8_bf16(p, 1, (tok * p.H + h) * p.D + 8 * c8);
+    }
+    e[i][0] = v.x; e[i][1] = v.y; e[i][2] = v.z; e[i][3] = v.w;
+  }
+  const int slot = slot_of(p, p.frame0 + j);
+  const long long vrow0 = ((long long)h * p.n_slots + slot) * p.D + 8 * c8;
+#pragma unroll
+  for (int dd = 0; dd < 8; ++dd) {   // dimension 8*c8+dd across the 8 tokens
+    uint32_t w[4];
+#pragma unroll
+    for (int t2 = 0; t2 < 4; ++t2) {
+      const uint32_t lo = (e[2 * t2][dd >> 1] >> (16 * (dd & 1))) & 0xFFFFu;
+      const uint32_t hi = (e[2 * t2 + 1][dd >> 1] >> (16 * (dd & 1))) & 0xFFFFu;
+      w[t2] = lo | (hi << 16);
+    }
+    *(uint4 *)(p.codes[1] + ((vrow0 + dd) * p.Tv + 8 * g8) * 2) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 __global__ void reset_kernel(int32_t *slot_frame, int32_t *slot_shot, float *kt, float *vt, int n) {
   const int i = threadIdx.x;
   if (i < n) {
@@ -273,6 +357,15 @@ hipError_t launch_cache_reset(const fp4kv_cache &c, hipStream_t s) {
 
 hipError_t launch_append(const AppendParams &p_in, hipStream_t s) {
   AppendParams p = p_in;
+  if (p.bf16_cache) {
+    const long long k_units = (long long)p.n_frames * p.Tc * p.H * (p.D >> 3);
+    const long long v_units = (long long)p.H * p.n_frames * (p.D >> 3) * (p.Tv >> 3);
+    p.v_blocks = (int)((v_units + kThreads - 1) / kThreads);
+    const long long k_blocks = (k_units + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(store_bf16_kernel, dim3((unsigned)(p.v_blocks + k_blocks)), dim3(kThreads),
+                       0, s, p);
+    return hipGetLastError();
+  }
   const long long k_units = (long long)p.H * p.n_frames * p.Tc * (p.D >> 4);
   const long long v_units = (long long)p.H * p.n_frames * (p.Tv >> 3) * (p.D >> 4);
   p.v_blocks = (int)((v_units + kThreads - 1) / kThreads);

@@ -58,6 +58,8 @@ extern "C" {
 
 /* Format tag of the NVFP4 cache layout described below. */
 #define FP4KV_FORMAT_NVFP4_V1 0x3146564Eu
+/* Baseline format: keys and values kept as bf16 (see fp4kv_cache). */
+#define FP4KV_FORMAT_BF16_V1  0x36314642u
 
 /* Limits.  Frames per call and cache slots are passed to kernels by value. */
 #define FP4KV_MAX_FRAMES 64   /* frames per append or attention call      */
@@ -99,9 +101,18 @@ extern "C" {
  *   slot_shot           int32 [S+W]     shot id of that frame
  * A decoded element is sign * E2M1(code) * E4M3(scale) * tensor_scale.
  * These buffers are opaque bytes: never cast or convert them.
+ *
+ * Baseline format FP4KV_FORMAT_BF16_V1 (the unquantized cache that NVFP4 is
+ * measured against; same ring, slots and attention): k_codes holds bf16
+ * [H][S+W][Tc][D], v_codes bf16 [H][S+W][D][Tv] (padding tokens zero),
+ * k_scales and v_scales are not used (0 bytes, may be NULL), and the tensor
+ * scales are written as 1.  The append rounds its inputs to bf16 (nearest
+ * even) and ignores tscale_in.  Attention converts the bf16 values to f16
+ * MFMA operands, so they must lie within the f16 range (|x| <= 65504);
+ * values below 2^-14 lose precision as f16 subnormals.
  */
 typedef struct fp4kv_cache {
-  uint32_t format_tag;        /* FP4KV_FORMAT_NVFP4_V1                        */
+  uint32_t format_tag;        /* FP4KV_FORMAT_NVFP4_V1 (or _BF16_V1)          */
   int32_t  n_heads;           /* H >= 1                                      */
   int32_t  head_dim;          /* D: 64 or 128                                */
   int32_t  tokens_per_frame;  /* T >= 1                                      */

@@ -182,3 +182,50 @@ class OracleCache:
         if return_probs:
             return out, probs
         return out
+
+
+# ------------------------------------------------------------ bf16 baseline
+def bf16_round(x):
+    """float32 -> the nearest bf16 value (ties to even), kept as float32.
+    Finite inputs only."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+class OracleCacheBF16(OracleCache):
+    """The unquantized baseline the NVFP4 cache is measured against: the same
+    ring of sink + window slots, keys and values kept as bf16 (rounded to
+    nearest even at append), tensor scales 1.
+
+    Layout (the library's FP4KV_FORMAT_BF16_V1), as float32 values here:
+      k_vals  [H][S+W][Tc][D]   keys, token-major
+      v_vals  [H][S+W][D][Tv]   values, dimension-major; padding tokens zero
+    """
+
+    def __init__(self, *a, **kw):
+        super().__init__(*a, **kw)
+        n = self.S + self.W
+        self.k_vals = np.zeros((self.H, n, self.Tc, self.D), np.float32)
+        self.v_vals = np.zeros((self.H, n, self.D, self.Tv), np.float32)
+
+    def append(self, k, v, frame0, n_frames, shots, tscale=None):
+        for idx, x in enumerate((k, v)):
+            xk = bf16_round(self.kept(x, n_frames))             # [n][Tc][H][D]
+            for j in range(n_frames):
+                slot = ring.slot_of(frame0 + j, self.S, self.W)
+                if idx == 0:
+                    self.k_vals[:, slot] = xk[j].transpose(1, 0, 2)
+                else:
+                    self.v_vals[:, slot] = 0.0
+                    self.v_vals[:, slot, :, :self.Tc] = xk[j].transpose(1, 2, 0)
+        for j in range(n_frames):
+            slot = ring.slot_of(frame0 + j, self.S, self.W)
+            self.k_tscale[slot] = self.v_tscale[slot] = 1.0
+            self.slot_frame[slot] = frame0 + j
+            self.slot_shot[slot] = shots[j]
+        return (np.float32(1.0), np.float32(1.0))
+
+    def decode_slot(self, slot):
+        return (self.k_vals[:, slot].copy(),
+                self.v_vals[:, slot, :, :self.Tc].transpose(0, 2, 1).copy())

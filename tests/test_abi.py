@@ -107,6 +107,17 @@ def test_descriptor_validation(field, value, status):
     assert lib.fp4kv_cache_nbytes(ctypes.byref(c), out) == status
 
 
+def test_bf16_format_sizes():
+    lib = _lib.load()
+    c = _desc(format_tag=_lib.FP4KV_FORMAT_BF16_V1)
+    out = (ctypes.c_size_t * 6)()
+    assert lib.fp4kv_cache_nbytes(ctypes.byref(c), out) == 0
+    H, n, Tc, Tv, D = 2, 15, 32, 32, 128
+    assert list(out) == [H * n * Tc * D * 2, H * n * D * Tv * 2, 0, 0, n * 4, n * 4]
+    c = _desc(format_tag=0x12345678)
+    assert lib.fp4kv_cache_nbytes(ctypes.byref(c), out) == _lib.FP4KV_EFORMAT
+
+
 def test_stride_must_divide_tokens():
     lib = _lib.load()
     out = (ctypes.c_size_t * 6)()
