@@ -117,8 +117,17 @@ int fp4kv_quantize_append(const fp4kv_cache *c, const void *k, const void *v, in
   if ((st = check_buffers(c))) return st;
   if (!k || !v || !frame_shot || !workspace) return FP4KV_EINVAL;
   if (in_dtype != FP4KV_F32 && in_dtype != FP4KV_BF16) return FP4KV_EINVAL;
-  if (frame0 < 0 || n_frames < 1 || n_frames > c->chunk_frames || n_frames > FP4KV_MAX_FRAMES)
-    return FP4KV_EINVAL;
+  if (frame0 < 0 || n_frames < 1 || n_frames > FP4KV_MAX_FRAMES) return FP4KV_EINVAL;
+  {  // the frames must land in distinct slots (a chunk, or a bulk re-append)
+    uint64_t used = 0;
+    const int S = c->sink_frames, W = c->window_frames;
+    for (int j = 0; j < n_frames; ++j) {
+      const long long f = (long long)frame0 + j;
+      const int slot = f < S ? (int)f : S + (int)((f - S) % W);
+      if (used >> slot & 1ull) return FP4KV_EINVAL;
+      used |= 1ull << slot;
+    }
+  }
   if ((long long)frame0 + n_frames > (1ll << 30)) return FP4KV_EINVAL;
   if (workspace_bytes < kWsBytes) return FP4KV_ESHAPE;
   if (!aligned16(k) || !aligned16(v) || !aligned16(workspace)) return FP4KV_EALIGN;

@@ -161,7 +161,11 @@ size_t fp4kv_append_workspace_bytes(void);
  *   k, v        device, [n_frames * T][H][D] of in_dtype (FP4KV_F32 or
  *               FP4KV_BF16), 16-byte aligned.  Only kept tokens are read.
  *   frame0      >= 0, first frame of the chunk.
- *   n_frames    1 .. min(C, FP4KV_MAX_FRAMES) (a partial last chunk is allowed).
+ *   n_frames    1 .. FP4KV_MAX_FRAMES, frames that land in distinct slots:
+ *               a chunk (a partial last chunk is allowed), or a bulk
+ *               re-append of cached frames (KV-recache: e.g. the sink frames
+ *               0..S-1 in one call, the window frames in another), which
+ *               share one tensor scale per call.
  *   frame_shot  host [n_frames]: shot id of each frame (written to slot_shot).
  *   tscale_in   device float[2] = {g_k, g_v} to use as tensor scales (finite,
  *               > 0), or NULL to compute g = amax / 2688 over the kept tokens

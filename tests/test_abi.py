@@ -138,7 +138,8 @@ def test_append_validation_before_launch():
     assert call(k=None) == -1
     assert call(dt=7) == -1
     assert call(n=0) == -1
-    assert call(n=4) == -1            # more than a chunk
+    assert call(f0=3, n=13) == -1     # frames 3 and 15 share a window slot
+    assert call(f0=0, n=16) == -1     # sink + window + one more
     assert call(f0=-1) == -1
     assert call(wsb=ws - 1) == -2
     assert call(k=A + 8) == -3

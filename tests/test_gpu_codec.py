@@ -156,3 +156,36 @@ def test_workspace_needs_no_initialization():
     api.quantize_append(gc, device_tensor(k, kb), device_tensor(v, vb), 0, 2, [0, 0])
     oc.append(k, v, 0, 2, [0, 0])
     assert not compare_cache(gc, oc)
+
+
+def test_bulk_reappend_kv_recache():
+    """KV-recache: after the ring has wrapped, the cached frames are
+    re-appended in bulk (the sink in one call, the whole window in another,
+    each with one tensor scale); the cache stays bit-exact with the oracle
+    and attention over it stays within the bar."""
+    from fp4_kv_cache_fp4kv_amd import api
+    from streams import err_stats, say
+    w = wl.Workload("recache", H=2, D=128, T=100, C=3, S=1, W=6, n_frames=12, seed=31,
+                    outlier_p=0.01, outlier_scale=20.0)
+    gc, oc = gpu_cache(w), OracleCache.for_workload(w)
+    for c in range(w.n_chunks):
+        f0, n = w.chunk_frames(c)
+        (_, _), (k, kb), (v, vb) = step_inputs(w, c)
+        api.quantize_append(gc, device_tensor(k, kb), device_tensor(v, vb), f0, n, [0] * n)
+        oc.append(k, v, f0, n, [0] * n)
+    f1 = w.n_frames
+    for f0, n in ((0, w.S), (f1 - w.W, w.W)):     # sink frames, then the window
+        say(f"recache frames {f0}..{f0 + n - 1}")
+        k, kb = wl.draw(w, 100 + f0, wl.K_ID, n_tokens=n * w.T)
+        v, vb = wl.draw(w, 100 + f0, wl.V_ID, n_tokens=n * w.T)
+        api.quantize_append(gc, device_tensor(k, kb), device_tensor(v, vb), f0, n, [0] * n)
+        oc.append(k, v, f0, n, [0] * n)
+        assert not compare_cache(gc, oc), (f0, n)
+    q, qb = wl.draw(w, w.n_chunks - 1, wl.Q_ID)
+    f0 = f1 - w.C
+    qr = api.rope_rel(device_tensor(q, qb), api.cache_positions(w.S, w.W, f0, w.C), w.T,
+                      gc.cos_sin)
+    o = api.attention_chunk(gc, qr, f0, w.C, [0] * w.C, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    mx, mn = err_stats(o.cpu().numpy(), oc.attention(q, f0, w.C, [0] * w.C))
+    assert mx <= 1e-2 and mn <= 1e-3, (mx, mn)
