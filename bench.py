@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--workload", default="l13b")
     ap.add_argument("--kv", default="nvfp4", choices=("nvfp4", "bf16"),
                     help="cache format: NVFP4 (the path) or the bf16 baseline")
+    ap.add_argument("--sink-per-shot", action="store_true",
+                    help="per-shot attention sinks (each shot re-anchors the sink)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters")
@@ -117,6 +119,28 @@ def cpu_baseline(w):
                       f"{dt:.1f} s"}
 
 
+def visible_pairs(w, f0, per_shot, shot_start):
+    """Number of (query frame, key frame) pairs attended at the chunk step
+    starting at frame f0 (sink + window, block-causal and shot masks)."""
+    f1 = f0 + w.C
+    ws = max(w.S, f1 - w.W)
+    n = 0
+    for qf in range(f0, f1):
+        for kf in range(f1):
+            if kf // w.C > qf // w.C:
+                continue
+            same = w.shot_of(kf) == w.shot_of(qf)
+            if per_shot:
+                rel = kf - shot_start(kf)
+                # the sink slot of a frame is taken over by a later shot's
+                later = any(g - shot_start(g) == rel for g in range(kf + 1, f1)) if rel < w.S else False
+                ok = same and ((rel < w.S and not later) or (rel >= w.S and kf >= ws))
+            else:
+                ok = (kf < w.S) or (kf >= ws and same)
+            n += ok
+    return n
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -136,7 +160,13 @@ def main():
     w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     gc = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride, device="cuda:0",
-                        kv_format=args.kv)
+                        kv_format=args.kv, sink_per_shot=args.sink_per_shot)
+
+    def shot_start(f):
+        s0 = w.shot_of(f)
+        while f > 0 and w.shot_of(f - 1) == s0:
+            f -= 1
+        return f
 
     def dev_t(vals, bits):
         if bits is not None:
@@ -159,13 +189,20 @@ def main():
         q, k, v = sets[c % n_sets]
         f0 = c * w.C
         shots = [w.shot_of(f) for f in range(f0, f0 + w.C)]
+        fss = [shot_start(f) for f in range(f0, f0 + w.C)] if args.sink_per_shot else None
         if record:
             e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             e[0].record()
-        api.quantize_append(gc, k, v, f0, w.C, shots)
+        api.quantize_append(gc, k, v, f0, w.C, shots, shot_starts=fss)
         if record:
             e[1].record()
-        api.rope_rel(q, api.cache_positions(w.S, w.W, f0, w.C), w.T, gc.cos_sin, out=qrot)
+        if fss is None:
+            api.rope_rel(q, api.cache_positions(w.S, w.W, f0, w.C), w.T, gc.cos_sin, out=qrot)
+        else:   # per-frame positions (a cut inside the chunk breaks the sequence)
+            for j in range(w.C):
+                rows = slice(j * w.T, (j + 1) * w.T)
+                api.rope_rel(q[rows], api.frame_position(w.S, w.W, f0 + j, f0 + w.C, fss[j]),
+                             w.T, gc.cos_sin, out=qrot[rows])
         if record:
             e[2].record()
         api.attention_chunk(gc, qrot, f0, w.C, shots, out=out)
@@ -196,7 +233,11 @@ def main():
     pct = lambda v, q: v[min(len(v) - 1, int(q * len(v)))]
 
     Nq, Nk = w.C * w.T, (w.S + w.W) * w.Tc
-    flops = 4.0 * w.H * Nq * Nk * w.D
+    # useful FLOP: only the (query frame, key frame) pairs the masks keep,
+    # averaged over the timed steps (equal to 4 H Nq Nk D without shots)
+    pairs = [visible_pairs(w, (c - args.steps + i) * w.C, args.sink_per_shot, shot_start)
+             for i in range(args.steps)]
+    flops = 4.0 * w.H * w.T * w.Tc * w.D * sum(pairs) / len(pairs)
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     es = 2 if w.dtype == "bf16" else 4
     kept = 2 * w.C * w.Tc * w.H * w.D
@@ -227,7 +268,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": workload_desc(w), "kv_format": args.kv, "query_rows": Nq,
+        "config": {"workload": workload_desc(w), "kv_format": args.kv,
+                   "sink": "per_shot" if args.sink_per_shot else "stream", "query_rows": Nq,
                    "keys": Nk,
                    "frames_per_step": w.C, "attention_ms": round(attn_ms, 4),
                    "attention_ms_p10_p50_p90": [round(pct(attn_each, q), 4)

@@ -42,6 +42,7 @@ class CacheDesc(ctypes.Structure):
         ("sink_frames", ctypes.c_int32),
         ("window_frames", ctypes.c_int32),
         ("rot_dim", ctypes.c_int32),
+        ("sink_per_shot", ctypes.c_int32),
         ("k_codes", ctypes.c_void_p),
         ("v_codes", ctypes.c_void_p),
         ("k_scales", ctypes.c_void_p),
@@ -85,6 +86,7 @@ def load() -> ctypes.CDLL:
     lib.fp4kv_append_workspace_bytes.argtypes = []
     lib.fp4kv_append_workspace_bytes.restype = ctypes.c_size_t
     lib.fp4kv_quantize_append.argtypes = [P(CacheDesc), vp, vp, c_int, c_i32, c_i32, P(c_i32),
+                                          P(c_i32),
                                           vp, vp, ctypes.c_size_t, vp]
     lib.fp4kv_quantize_append.restype = c_int
     lib.fp4kv_rope_table.argtypes = [P(c_f), c_i32, c_i32, ctypes.c_double]

@@ -53,7 +53,8 @@ class FP4KVCache:
 
     def __init__(self, H: int, D: int, T: int, C: int, S: int, W: int,
                  token_stride: int = 1, rot_dim: Optional[int] = None,
-                 device: str = "cuda:0", kv_format: str = "nvfp4"):
+                 device: str = "cuda:0", kv_format: str = "nvfp4",
+                 sink_per_shot: bool = False):
         lib = load()
         if kv_format not in ("nvfp4", "bf16"):
             raise ValueError("kv_format must be 'nvfp4' or 'bf16'")
@@ -66,7 +67,9 @@ class FP4KVCache:
         tag = _lib.FP4KV_FORMAT_NVFP4_V1 if kv_format == "nvfp4" else _lib.FP4KV_FORMAT_BF16_V1
         self.desc = CacheDesc(format_tag=tag, n_heads=H, head_dim=D,
                               tokens_per_frame=T, token_stride=token_stride, chunk_frames=C,
-                              sink_frames=S, window_frames=W, rot_dim=self.rot_dim)
+                              sink_frames=S, window_frames=W, rot_dim=self.rot_dim,
+                              sink_per_shot=int(bool(sink_per_shot)))
+        self.sink_per_shot = bool(sink_per_shot)
         sizes = (ctypes.c_size_t * 6)()
         check(lib.fp4kv_cache_nbytes(ctypes.byref(self.desc), sizes), "fp4kv_cache_nbytes")
         self.Tv = -(-self.Tc // 32) * 32
@@ -126,8 +129,10 @@ def rope_table(n_pos: int, rot_dim: int, base: float = 10000.0) -> torch.Tensor:
 
 def quantize_append(cache: FP4KVCache, k: torch.Tensor, v: torch.Tensor, frame0: int,
                     n_frames: int, shots: Sequence[int],
-                    tscale: Optional[torch.Tensor] = None) -> None:
-    """fp4kv_quantize_append on the current stream."""
+                    tscale: Optional[torch.Tensor] = None,
+                    shot_starts: Optional[Sequence[int]] = None) -> None:
+    """fp4kv_quantize_append on the current stream.  shot_starts (first frame
+    of each frame's shot) is required by a cache with per-shot sinks."""
     for t, nm in ((k, "k"), (v, "v")):
         _require(t, nm, device=cache.device)
     if k.dtype != v.dtype or k.dtype not in _DTYPES:
@@ -140,7 +145,8 @@ def quantize_append(cache: FP4KVCache, k: torch.Tensor, v: torch.Tensor, frame0:
         _require(tscale, "tscale", torch.float32, cache.device)
     st = load().fp4kv_quantize_append(
         ctypes.byref(cache.desc), k.data_ptr(), v.data_ptr(), _DTYPES[k.dtype], frame0, n_frames,
-        _i32_array(shots), _ptr(tscale), cache.workspace.data_ptr(), cache.workspace.numel(),
+        _i32_array(shots), None if shot_starts is None else _i32_array(shot_starts),
+        _ptr(tscale), cache.workspace.data_ptr(), cache.workspace.numel(),
         _stream(cache.device))
     check(st, "fp4kv_quantize_append")
 
@@ -200,6 +206,15 @@ def attention_chunk(cache: FP4KVCache, q_rot: torch.Tensor, q_frame0: int, n_q_f
         _stream(cache.device))
     check(st, "fp4kv_attention_chunk")
     return out
+
+
+def frame_position(S: int, W: int, f: int, f1: int, shot_start: Optional[int] = None) -> int:
+    """Cache-relative position of frame f at a step ending at frame f1: with
+    per-shot sinks (shot_start given) f - shot_start inside the shot's first
+    S frames, else S + f - max(S, f1 - W); without, f for f < S."""
+    ws = max(S, f1 - W)
+    rel = f if shot_start is None else f - shot_start
+    return rel if rel < S else S + (f - ws)
 
 
 def cache_positions(S: int, W: int, f0: int, n: int) -> int:

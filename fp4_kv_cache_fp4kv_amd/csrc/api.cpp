@@ -14,7 +14,7 @@ using namespace fp4kv;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -37,6 +37,7 @@ int check_shape(const fp4kv_cache *c) {
   if (c->window_frames < c->chunk_frames) return FP4KV_ESHAPE;
   if (c->sink_frames + c->window_frames > FP4KV_MAX_SLOTS) return FP4KV_ESHAPE;
   if (c->rot_dim < 0 || c->rot_dim > c->head_dim || (c->rot_dim & 1)) return FP4KV_EINVAL;
+  if (c->sink_per_shot != 0 && c->sink_per_shot != 1) return FP4KV_EINVAL;
   const long long rows = (long long)c->n_heads * (c->sink_frames + c->window_frames) *
                          (c->tokens_per_frame / c->token_stride);
   if (rows * c->head_dim > (1ll << 40)) return FP4KV_ESHAPE;
@@ -110,22 +111,30 @@ size_t fp4kv_append_workspace_bytes(void) { return kWsBytes; }
 
 int fp4kv_quantize_append(const fp4kv_cache *c, const void *k, const void *v, int in_dtype,
                           int32_t frame0, int32_t n_frames, const int32_t *frame_shot,
-                          const float *tscale_in, void *workspace, size_t workspace_bytes,
-                          void *stream) {
+                          const int32_t *frame_shot_start, const float *tscale_in,
+                          void *workspace, size_t workspace_bytes, void *stream) {
   int st = check_shape(c);
   if (st) return st;
   if ((st = check_buffers(c))) return st;
   if (!k || !v || !frame_shot || !workspace) return FP4KV_EINVAL;
   if (in_dtype != FP4KV_F32 && in_dtype != FP4KV_BF16) return FP4KV_EINVAL;
   if (frame0 < 0 || n_frames < 1 || n_frames > FP4KV_MAX_FRAMES) return FP4KV_EINVAL;
+  if (c->sink_per_shot && !frame_shot_start) return FP4KV_EINVAL;
+  int32_t slots[FP4KV_MAX_FRAMES];
   {  // the frames must land in distinct slots (a chunk, or a bulk re-append)
     uint64_t used = 0;
     const int S = c->sink_frames, W = c->window_frames;
     for (int j = 0; j < n_frames; ++j) {
       const long long f = (long long)frame0 + j;
-      const int slot = f < S ? (int)f : S + (int)((f - S) % W);
+      long long rel = f;   // index from the sink's anchor frame
+      if (c->sink_per_shot) {
+        if (frame_shot_start[j] < 0 || frame_shot_start[j] > f) return FP4KV_EINVAL;
+        rel = f - frame_shot_start[j];
+      }
+      const int slot = rel < S ? (int)rel : S + (int)((f - S) % W);
       if (used >> slot & 1ull) return FP4KV_EINVAL;
       used |= 1ull << slot;
+      slots[j] = slot;
     }
   }
   if ((long long)frame0 + n_frames > (1ll << 30)) return FP4KV_EINVAL;
@@ -160,7 +169,10 @@ int fp4kv_quantize_append(const fp4kv_cache *c, const void *k, const void *v, in
   p.n_frames = n_frames;
   p.in_bf16 = in_dtype == FP4KV_BF16;
   p.bf16_cache = is_bf16(c);
-  for (int j = 0; j < n_frames; ++j) p.shot[j] = frame_shot[j];
+  for (int j = 0; j < n_frames; ++j) {
+    p.shot[j] = frame_shot[j];
+    p.slot[j] = slots[j];
+  }
   return from_hip(launch_append(p, (hipStream_t)stream));
 }
 
@@ -255,6 +267,7 @@ int fp4kv_attention_chunk(const fp4kv_cache *c, const void *q_rot, int q_dtype, 
   p.n_q_frames = n_q_frames;
   p.Nq = (int)nq;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.sink_per_shot = c->sink_per_shot;
   for (int j = 0; j < n_q_frames; ++j) p.q_shot[j] = q_shot[j];
 
   // Work split: equal ranges of the virtual key tiles (n_v per row block)

@@ -608,14 +608,20 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
       const int qf_hi = p.q_frame0 + (min(p.Nq, wg_row0 + kBM) - 1) / p.T;
       bool ok = false;
       int kf = -1, kshot = 0;
+      bool sink = false;
       if (lane < p.n_slots) {
         kf = p.slot_frame[lane];
         kshot = p.slot_shot[lane];
-        ok = kf >= 0 && kf < f1 && (kf < p.S || kf >= ws);
+        // a sink slot holds frame kf < S of the stream (seen across shots),
+        // or with per-shot sinks one of the first S frames of some shot
+        // (seen by that shot only); its position is its slot
+        sink = p.sink_per_shot ? lane < p.S : kf < p.S;
+        const bool exempt = sink && !p.sink_per_shot;
+        ok = kf >= 0 && kf < f1 && (sink || kf >= ws);
         if (ok) {
           bool any = false;
           for (int qf = qf_lo; qf <= qf_hi; ++qf)
-            any |= (kf / p.C <= qf / p.C) && (kf < p.S || kshot == p.q_shot[qf - p.q_frame0]);
+            any |= (kf / p.C <= qf / p.C) && (exempt || kshot == p.q_shot[qf - p.q_frame0]);
           ok = any;
         }
       }
@@ -624,7 +630,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
       if (ok) {
         sm.fl_slot[idx] = lane;
         sm.fl_kf[idx] = kf;
-        sm.fl_pos[idx] = kf < p.S ? kf : p.S + (kf - ws);
+        sm.fl_pos[idx] = sink ? lane : p.S + (kf - ws);
         sm.fl_shot[idx] = kshot;
         sm.fl_gk[idx] = p.k_tscale[lane];
         sm.fl_gv[idx] = p.v_tscale[lane];
@@ -731,7 +737,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
       float f_cf = 0.0f, f_gv = 1.0f, f_ratio = 1.0f;
       auto load_frame = [&](int fi) __attribute__((always_inline)) {
         const int kf = sm.fl_kf[fi];
-        f_vis = row_ok & (kf / p.C <= my_qchunk) & ((kf < p.S) | (sm.fl_shot[fi] == my_qshot));
+        f_vis = row_ok & (kf / p.C <= my_qchunk) &
+                ((!p.sink_per_shot & (kf < p.S)) | (sm.fl_shot[fi] == my_qshot));
         f_all = __ballot(f_vis) == ~0ull;
         f_cf = p.scale_log2 * sm.fl_gk[fi];
         const float gv = sm.fl_gv[fi];

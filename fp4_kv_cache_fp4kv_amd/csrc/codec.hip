@@ -162,9 +162,8 @@ __device__ __forceinline__ void load_block(const AppendParams &p, int y, long lo
   }
 }
 
-__device__ __forceinline__ int slot_of(const AppendParams &p, int f) {
-  return f < p.S ? f : p.S + (f - p.S) % p.W;
-}
+// Slot of appended frame j (computed on the host for either sink mode).
+__device__ __forceinline__ int slot_of(const AppendParams &p, int j) { return p.slot[j]; }
 
 // One launch encodes both tensors.  Workgroups [0, p.v_blocks) encode the
 // values, dimension-major: one thread per (8 tokens, 16-block) writes one
@@ -183,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(AppendParams p) {
 
   if ((blockIdx.x == 0 || (int)blockIdx.x == p.v_blocks) && threadIdx.x < p.n_frames) {
     const int j = threadIdx.x, f = p.frame0 + j;
-    const int slot = slot_of(p, f);
+    const int slot = slot_of(p, j);
     p.tscale[y][slot] = g;
     if (y == 0) {
       p.slot_frame[slot] = f;
@@ -201,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(AppendParams p) {
     rest /= p.Tc;
     const int j = (int)(rest % p.n_frames);
     const int h = (int)(rest / p.n_frames);
-    const int slot = slot_of(p, p.frame0 + j);
+    const int slot = slot_of(p, j);
     const long long tok = (long long)j * p.T + (long long)tc * p.stride;
     float x[16];
     load_block(p, 0, (tok * p.H + h) * p.D + b * 16, x);
@@ -223,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(AppendParams p) {
   rest /= groups;
   const int j = (int)(rest % p.n_frames);
   const int h = (int)(rest / p.n_frames);
-  const int slot = slot_of(p, p.frame0 + j);
+  const int slot = slot_of(p, j);
   uint32_t rows[16];                                         // one word per dimension
 #pragma unroll
   for (int r = 0; r < 16; ++r) rows[r] = 0u;
@@ -280,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void store_bf16_kernel(AppendParams p) {
     const uint32_t units = (uint32_t)(p.n_frames * p.Tc * p.H * n8);
     const uint32_t u = (blockIdx.x - p.v_blocks) * kThreads + threadIdx.x;
     if ((int)blockIdx.x == p.v_blocks && threadIdx.x < p.n_frames) {
-      const int j = threadIdx.x, f = p.frame0 + j, sl = slot_of(p, f);
+      const int j = threadIdx.x, f = p.frame0 + j, sl = slot_of(p, j);
       p.tscale[0][sl] = 1.0f;
       p.tscale[1][sl] = 1.0f;
       p.slot_frame[sl] = f;
@@ -295,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void store_bf16_kernel(AppendParams p) {
     const int j = (int)(rest / p.Tc);
     const long long tok = (long long)j * p.T + (long long)tc * p.stride;
     const uint4 v = load8_bf16(p, 0, (tok * p.H + h) * p.D + 8 * c8);
-    const int slot = slot_of(p, p.frame0 + j);
+    const int slot = slot_of(p, j);
     const long long row = ((long long)h * p.n_slots + slot) * p.Tc + tc;
     *(uint4 *)(p.codes[0] + (row * p.D + 8 * c8) * 2) = v;
     return;
@@ -321,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void store_bf16_kernel(AppendParams p) {
     }
     e[i][0] = v.x; e[i][1] = v.y; e[i][2] = v.z; e[i][3] = v.w;
   }
-  const int slot = slot_of(p, p.frame0 + j);
+  const int slot = slot_of(p, j);
   const long long vrow0 = ((long long)h * p.n_slots + slot) * p.D + 8 * c8;
 #pragma unroll
   for (int dd = 0; dd < 8; ++dd) {   // dimension 8*c8+dd across the 8 tokens

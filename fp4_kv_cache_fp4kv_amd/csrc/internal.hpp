@@ -28,6 +28,7 @@ struct AppendParams {
   int bf16_cache;          // FP4KV_FORMAT_BF16_V1: store bf16, no quantization
   int v_blocks;            // workgroups of the value pass in encode_kernel
   int32_t shot[FP4KV_MAX_FRAMES];
+  int32_t slot[FP4KV_MAX_FRAMES];   // cache slot of each frame (host-computed)
 };
 
 struct RopeParams {
@@ -48,6 +49,7 @@ struct AttnParams {
   int H, T, Tc, Tv, C, S, W, n_slots, rot_dim;
   int q_frame0, n_q_frames, Nq, q_f32;
   int bf16_cache;          // keys and values are bf16 (FP4KV_FORMAT_BF16_V1)
+  int sink_per_shot;       // sink slots hold the first S frames of each shot
   float scale_log2;        // softmax_scale * log2(e)
   int n_wg;                // workgroups of the split schedule
   float *ws_o;             // partial g_v * acc [2 n_wg][256 rows][D]

@@ -72,6 +72,17 @@ extern "C" {
  * The cache holds S sink frames (the first S frames of the stream, never
  * evicted) and a ring of W window frames that includes the current chunk:
  * frame f lives in slot f if f < S, else in slot S + ((f - S) mod W).
+ *
+ * Per-shot sink (sink_per_shot = 1; the other reading of the multi-shot
+ * attention sink, evermx.com "Multi-Shot Generation"): every shot re-anchors
+ * the sink to its own first S frames.  Frame f of a shot starting at frame
+ * fs lives in sink slot f - fs if f - fs < S (replacing the previous shot's
+ * sink frame), else in slot S + ((f - S) mod W).  A sink slot is visible
+ * only to queries of its own shot, at position f - fs; a cut inside a chunk
+ * therefore leaves the earlier shot's frames of that chunk without a sink.
+ * Queries of a frame qf are rotated by qf - fs if qf - fs < S, else by
+ * S + (qf - ws), which need not be consecutive within a chunk (rotate each
+ * frame with its own pos0).
  * Each cached frame keeps Tc = tokens_per_frame / token_stride tokens
  * (in-frame token t is kept iff t mod token_stride == 0).
  *
@@ -121,6 +132,7 @@ typedef struct fp4kv_cache {
   int32_t  sink_frames;       /* S >= 0                                      */
   int32_t  window_frames;     /* W >= C; S + W <= FP4KV_MAX_SLOTS            */
   int32_t  rot_dim;           /* even, 0 <= rot_dim <= D: rotated leading dims */
+  int32_t  sink_per_shot;     /* 0: stream sink; 1: per-shot sink (see below)  */
   uint8_t *k_codes, *v_codes;
   uint8_t *k_scales, *v_scales;
   float   *k_tscale, *v_tscale;
@@ -167,6 +179,9 @@ size_t fp4kv_append_workspace_bytes(void);
  *               0..S-1 in one call, the window frames in another), which
  *               share one tensor scale per call.
  *   frame_shot  host [n_frames]: shot id of each frame (written to slot_shot).
+ *   frame_shot_start  host [n_frames]: first frame of each frame's shot
+ *               (0 <= start <= frame), used when sink_per_shot = 1 (it picks
+ *               the slot); may be NULL otherwise.
  *   tscale_in   device float[2] = {g_k, g_v} to use as tensor scales (finite,
  *               > 0), or NULL to compute g = amax / 2688 over the kept tokens
  *               of each of K and V (g = 1 when amax = 0).
@@ -185,8 +200,9 @@ size_t fp4kv_append_workspace_bytes(void);
  */
 int fp4kv_quantize_append(const fp4kv_cache *c, const void *k, const void *v,
                           int in_dtype, int32_t frame0, int32_t n_frames,
-                          const int32_t *frame_shot, const float *tscale_in,
-                          void *workspace, size_t workspace_bytes, void *stream);
+                          const int32_t *frame_shot, const int32_t *frame_shot_start,
+                          const float *tscale_in, void *workspace, size_t workspace_bytes,
+                          void *stream);
 
 /*
  * fp4kv_rope_table - fill a rotary table on the host (no GPU):

@@ -65,3 +65,31 @@ def key_visible(kf: int, qf: int, f1: int, S: int, W: int, C: int,
     if chunk_of(kf, C) > chunk_of(qf, C):
         return False
     return kf < S or shot_k == shot_q
+
+
+# ---------------------------------------------------- per-shot sink variant
+# The other reading of the multi-shot attention sink (evermx.com,
+# "Multi-Shot Generation"; hysenlabs.com lists a "multi-shot attention
+# sink"): each shot re-anchors the sink to its own first S frames.
+#   * frame f of a shot that starts at frame fs is a sink frame of that shot
+#     iff f - fs < S; it lives in sink slot f - fs (replacing the previous
+#     shot's), all other frames in window slot S + ((f - S) mod W);
+#   * ws = max(S, f1 - W) as above; a sink slot is visible to query frame qf
+#     iff it holds a frame of qf's shot; a window slot iff its frame is in
+#     [ws, f1) and of qf's shot; block-causal as above;
+#   * positions: a sink frame's position is its slot (f - fs); any other
+#     frame's is S + (f - ws); queries likewise.
+
+def slot_of_shot(f: int, fs: int, S: int, W: int) -> int:
+    return f - fs if f - fs < S else S + (f - S) % W
+
+
+def pos_shot(f: int, fs: int, f1: int, S: int, W: int) -> int:
+    return f - fs if f - fs < S else S + (f - window_start(f1, S, W))
+
+
+def key_visible_shot(kf: int, kslot: int, qf: int, f1: int, S: int, W: int, C: int,
+                     shot_k: int, shot_q: int) -> bool:
+    if not (0 <= kf < f1) or shot_k != shot_q or chunk_of(kf, C) > chunk_of(qf, C):
+        return False
+    return kslot < S or kf >= window_start(f1, S, W)

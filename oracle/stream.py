@@ -48,13 +48,14 @@ from . import rope
 
 class OracleCache:
     def __init__(self, H, D, T, C, S, W, token_stride=1, rot_dim=None,
-                 base=10000.0):
+                 base=10000.0, sink_per_shot=False):
         assert T % token_stride == 0 and D % nvfp4.BLOCK == 0
         self.H, self.D, self.T, self.C, self.S, self.W = H, D, T, C, S, W
         self.stride = token_stride
         self.Tc = T // token_stride
         self.rot_dim = D if rot_dim is None else rot_dim
         self.base = base
+        self.sink_per_shot = sink_per_shot   # see ring.slot_of_shot
         n = S + W
         self.Tv = -(-self.Tc // 32) * 32
         self.k_codes = np.zeros((H, n, self.Tc, D // 2), np.uint8)
@@ -67,8 +68,15 @@ class OracleCache:
         self.slot_shot = np.zeros(n, np.int32)
 
     @classmethod
-    def for_workload(cls, w, rot_dim=None):
-        return cls(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride, rot_dim)
+    def for_workload(cls, w, rot_dim=None, sink_per_shot=False):
+        return cls(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride, rot_dim,
+                   sink_per_shot=sink_per_shot)
+
+    def slot(self, f, fs=0):
+        """Slot of frame f (fs: first frame of its shot, per-shot sinks)."""
+        if self.sink_per_shot:
+            return ring.slot_of_shot(f, fs, self.S, self.W)
+        return ring.slot_of(f, self.S, self.W)
 
     def snapshot(self):
         return copy.deepcopy(self)
@@ -79,16 +87,18 @@ class OracleCache:
         x = np.asarray(x, dtype=np.float32).reshape(n_frames, self.T, self.H, self.D)
         return x[:, ::self.stride]
 
-    def append(self, k, v, frame0, n_frames, shots, tscale=None):
+    def append(self, k, v, frame0, n_frames, shots, tscale=None, shot_starts=None):
         """Quantize K, V ([n_frames*T][H][D], float32 values) into the slots of
-        frames frame0 .. frame0+n_frames-1.  Returns (g_k, g_v)."""
+        frames frame0 .. frame0+n_frames-1 (shot_starts: first frame of each
+        frame's shot, per-shot sinks only).  Returns (g_k, g_v)."""
+        fss = [0] * n_frames if shot_starts is None else list(shot_starts)
         gs = []
         for idx, (x, tsc) in enumerate(((k, self.k_tscale), (v, self.v_tscale))):
             xk = self.kept(x, n_frames)                        # [n][Tc][H][D]
             g = nvfp4.tensor_scale(xk) if tscale is None else np.float32(tscale[idx])
             c, s8 = nvfp4.encode_blocks(xk, g)                 # codes per element
             for j in range(n_frames):
-                slot = ring.slot_of(frame0 + j, self.S, self.W)
+                slot = self.slot(frame0 + j, fss[j])
                 cj = c[j].transpose(1, 0, 2)                   # [H][Tc][D]
                 sj = s8[j].transpose(1, 0, 2)                  # [H][Tc][D/16]
                 if idx == 0:
@@ -103,7 +113,7 @@ class OracleCache:
                 tsc[slot] = g
             gs.append(g)
         for j in range(n_frames):
-            slot = ring.slot_of(frame0 + j, self.S, self.W)
+            slot = self.slot(frame0 + j, fss[j])
             self.slot_frame[slot] = frame0 + j
             self.slot_shot[slot] = shots[j]
         return tuple(gs)
@@ -119,14 +129,17 @@ class OracleCache:
         return kh, vh
 
     # ------------------------------------------------------------ positions
-    def positions(self, frames, f1):
+    def positions(self, frames, f1, shot_starts=None):
+        if self.sink_per_shot:
+            return np.array([ring.pos_shot(f, fs, f1, self.S, self.W)
+                             for f, fs in zip(frames, shot_starts)])
         return np.array([ring.rel_pos(f, f1, self.S, self.W) for f in frames])
 
-    def rope_queries(self, q, q_frame0, n_q_frames):
+    def rope_queries(self, q, q_frame0, n_q_frames, q_shot_starts=None):
         """Rotate q[n_q_frames*T][H][D] by the cache-relative positions of its
         frames; float64 result."""
         f1 = q_frame0 + n_q_frames
-        pos = self.positions(range(q_frame0, f1), f1)
+        pos = self.positions(range(q_frame0, f1), f1, q_shot_starts)
         pos_tok = np.repeat(pos, self.T)[:, None]           # [Nq, 1] over heads
         return rope.rotate(q, pos_tok, self.rot_dim, self.base)
 
@@ -136,12 +149,13 @@ class OracleCache:
         out = []
         for slot in range(self.S + self.W):
             kf = int(self.slot_frame[slot])
-            if 0 <= kf < f1 and (kf < self.S or kf >= ws):
+            sink = slot < self.S if self.sink_per_shot else kf < self.S
+            if 0 <= kf < f1 and (sink or kf >= ws):
                 out.append((slot, kf))
         return out
 
     def attention(self, q, q_frame0, n_q_frames, q_shots, scale=None,
-                  return_probs=False, rows=None, heads=None):
+                  return_probs=False, rows=None, heads=None, q_shot_starts=None):
         """Chunk attention for query frames q_frame0 .. +n_q_frames-1.
 
         q: float32 values [n_q_frames*T][H][D] before rotation.
@@ -153,22 +167,31 @@ class OracleCache:
         f1 = q_frame0 + n_q_frames
         rows = np.arange(n_q_frames * T) if rows is None else np.asarray(rows)
         heads = list(range(H)) if heads is None else list(heads)
-        qr = self.rope_queries(q, q_frame0, n_q_frames)[rows]  # [Nr][H][D]
+        qr = self.rope_queries(q, q_frame0, n_q_frames, q_shot_starts)[rows]  # [Nr][H][D]
+        ws = ring.window_start(f1, S, W)
         slots = self.visible_slots(f1)
         keys, vals, kpos = [], [], []
         for slot, kf in slots:
             kh, vh = self.decode_slot(slot)                    # [H][Tc][D]
             keys.append(kh)
             vals.append(vh)
-            kpos.append(np.full(self.Tc, ring.rel_pos(kf, f1, S, W)))
+            if self.sink_per_shot:
+                kpos.append(np.full(self.Tc, slot if slot < S else S + (kf - ws)))
+            else:
+                kpos.append(np.full(self.Tc, ring.rel_pos(kf, f1, S, W)))
         K = np.concatenate(keys, axis=1)                       # [H][Nk][D]
         V = np.concatenate(vals, axis=1)
         kpos = np.concatenate(kpos)
         frame_rows = {}
         for a, qf in enumerate(range(q_frame0, f1)):
-            per_slot = [ring.key_visible(kf, qf, f1, S, W, C,
-                                         int(self.slot_shot[slot]), int(q_shots[a]))
-                        for slot, kf in slots]
+            if self.sink_per_shot:
+                per_slot = [ring.key_visible_shot(kf, slot, qf, f1, S, W, C,
+                                                  int(self.slot_shot[slot]), int(q_shots[a]))
+                            for slot, kf in slots]
+            else:
+                per_slot = [ring.key_visible(kf, qf, f1, S, W, C,
+                                             int(self.slot_shot[slot]), int(q_shots[a]))
+                            for slot, kf in slots]
             frame_rows[a] = np.repeat(np.array(per_slot, dtype=bool), self.Tc)
         mask = np.stack([frame_rows[int(r) // T] for r in rows])
         out = np.empty((len(rows), len(heads), D), np.float64)
@@ -209,18 +232,19 @@ class OracleCacheBF16(OracleCache):
         self.k_vals = np.zeros((self.H, n, self.Tc, self.D), np.float32)
         self.v_vals = np.zeros((self.H, n, self.D, self.Tv), np.float32)
 
-    def append(self, k, v, frame0, n_frames, shots, tscale=None):
+    def append(self, k, v, frame0, n_frames, shots, tscale=None, shot_starts=None):
+        fss = [0] * n_frames if shot_starts is None else list(shot_starts)
         for idx, x in enumerate((k, v)):
             xk = bf16_round(self.kept(x, n_frames))             # [n][Tc][H][D]
             for j in range(n_frames):
-                slot = ring.slot_of(frame0 + j, self.S, self.W)
+                slot = self.slot(frame0 + j, fss[j])
                 if idx == 0:
                     self.k_vals[:, slot] = xk[j].transpose(1, 0, 2)
                 else:
                     self.v_vals[:, slot] = 0.0
                     self.v_vals[:, slot, :, :self.Tc] = xk[j].transpose(1, 2, 0)
         for j in range(n_frames):
-            slot = ring.slot_of(frame0 + j, self.S, self.W)
+            slot = self.slot(frame0 + j, fss[j])
             self.k_tscale[slot] = self.v_tscale[slot] = 1.0
             self.slot_frame[slot] = frame0 + j
             self.slot_shot[slot] = shots[j]

@@ -58,7 +58,7 @@ def _desc(**kw):
 
 def test_strerror_and_version():
     lib = _lib.load()
-    assert lib.fp4kv_abi_version() == 1
+    assert lib.fp4kv_abi_version() == 2
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.fp4kv_strerror(st)
     assert lib.fp4kv_append_workspace_bytes() >= 64
@@ -131,10 +131,11 @@ def test_append_validation_before_launch():
     shots = (ctypes.c_int32 * 4)(0, 0, 0, 0)
     ws = lib.fp4kv_append_workspace_bytes()
     A = 0x100000
+    starts = (ctypes.c_int32 * 4)(0, 0, 0, 0)
     call = lambda **kw: lib.fp4kv_quantize_append(
         ctypes.byref(kw.get("c", c)), kw.get("k", A), kw.get("v", A), kw.get("dt", 1),
-        kw.get("f0", 0), kw.get("n", 3), kw.get("shots", shots), None, kw.get("ws", A),
-        kw.get("wsb", ws), None)
+        kw.get("f0", 0), kw.get("n", 3), kw.get("shots", shots), kw.get("starts", None), None,
+        kw.get("ws", A), kw.get("wsb", ws), None)
     assert call(k=None) == -1
     assert call(dt=7) == -1
     assert call(n=0) == -1
@@ -145,6 +146,10 @@ def test_append_validation_before_launch():
     assert call(k=A + 8) == -3
     assert call(ws=A + 4) == -3
     assert call(shots=None) == -1
+    ps = _desc(sink_per_shot=1)
+    assert call(c=ps) == -1                     # per-shot sinks need shot starts
+    assert call(c=ps, f0=2, n=1, starts=(ctypes.c_int32 * 4)(3, 0, 0, 0)) == -1   # start > frame
+    assert call(c=_desc(sink_per_shot=2)) == -1
     bad = _desc()
     bad.k_codes = 0x10008
     assert call(c=bad) == -3
