@@ -26,9 +26,11 @@ formula.  Where they are silent each module states the reading it takes.
 Modules:
   nvfp4     E4M3 / E2M1 element codecs and the NVFP4 block encoder/decoder.
   ring      sink + sliding-window slot bookkeeping, positions and masks.
-  rope      rotary position rotation in float64.
+  rope      rotary position rotation in float64, and the float32 table and
+            rotation that keys stored rotated go through.
   attention float64 softmax attention over the decoded cache.
-  stream    a cache object that chains the above, in the library's layout.
+  stream    a cache object that chains the above, in the library's layout
+            (keys stored before rotation), and the rotate-at-write variant.
 
 Parity status: every function here is pinned by tests under tests/ against
 library routines, closed forms, invariants or brute force; none is marked

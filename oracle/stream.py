@@ -25,9 +25,11 @@ value entries of the padding tokens Tc..Tv-1 are zero.
   k_tscale, v_tscale float32 [S+W]    tensor scale g of the frame
   slot_frame         int32 [S+W]      frame held, -1 when empty
   slot_shot          int32 [S+W]      shot id of that frame
-The cache holds keys before rotation; keys are rotated after decoding with
-the positions of the current step, so codes are written once and never
+OracleCache holds keys before rotation; keys are rotated after decoding
+with the positions of the current step, so codes are written once and never
 re-quantized when the window slides (reading of "KV-cache relative RoPE").
+OracleCacheRot is the other reading: keys stored rotated and turned in place
+when the window slides.
 
 Keeping every token_stride-th token of each cached frame stands in for the
 pages' KV compression (refft.com, "TriAttention compression"); queries are
@@ -144,6 +146,11 @@ class OracleCache:
         return rope.rotate(q, pos_tok, self.rot_dim, self.base)
 
     # ------------------------------------------------------------ attention
+    def rotate_keys(self, k, kpos):
+        """Decoded keys [Nk][D] turned by their cache-relative positions
+        (float64): this cache stores keys before rotation."""
+        return rope.rotate(k, kpos, self.rot_dim, self.base)
+
     def visible_slots(self, f1):
         ws = ring.window_start(f1, self.S, self.W)
         out = []
@@ -197,7 +204,7 @@ class OracleCache:
         out = np.empty((len(rows), len(heads), D), np.float64)
         probs = []
         for hi, h in enumerate(heads):
-            kr = rope.rotate(K[h], kpos, self.rot_dim, self.base)
+            kr = self.rotate_keys(K[h], kpos)
             if return_probs:
                 s = (qr[:, h] @ kr.T) * (1.0 / np.sqrt(D) if scale is None else scale)
                 probs.append(att.softmax_rows(s, mask))
@@ -253,3 +260,76 @@ class OracleCacheBF16(OracleCache):
     def decode_slot(self, slot):
         return (self.k_vals[:, slot].copy(),
                 self.v_vals[:, slot, :, :self.Tc].transpose(0, 2, 1).copy())
+
+
+# ------------------------------------------------- rotate-at-write variant
+class OracleCacheRot(OracleCache):
+    """The other reading of "KV-cache relative RoPE" (refft.com, relative RoPE
+    and TriAttention question; aiany.app, "What Sets It Apart"): keys are
+    stored already rotated by their cache-relative position, and when the
+    window start moves the surviving window keys are turned back in place.
+
+    Reading, step by step:
+      * a key frame is written rotated by its position at the step that
+        appends it (window end f1 = the end of that step's frames): rotate in
+        float32 (rope.rotate_f32 with the float32 table), then NVFP4-encode
+        as any append (one tensor scale over the call's kept tokens);
+      * when the window end moves from f1_from to f1_to the window start
+        moves by delta = ws(f1_to) - ws(f1_from); every window slot (slot
+        >= S) whose frame f satisfies ws(f1_to) <= f < f1_from survives and
+        is turned by -delta: decode (float32), rotate_f32 inverse with table
+        row delta, encode again with a fresh tensor scale amax / 2688 over
+        that frame's kept keys (all heads); values and sink slots never
+        move (a sink frame's position is fixed);
+      * attention decodes keys and uses them as stored (no key rotation);
+        queries are rotated by their positions as before.
+    Each window key is re-encoded once per step it survives, up to
+    ceil(W / C) - 1 times in steady state: the re-quantization error is the
+    price of this reading.
+    """
+
+    def __init__(self, *a, table=None, **kw):
+        super().__init__(*a, **kw)
+        n = self.S + self.W
+        self.table = (rope.table_f32(n, self.rot_dim, self.base) if table is None
+                      else np.asarray(table, np.float32))
+
+    def rotate_keys(self, k, kpos):
+        return np.asarray(k, np.float64)
+
+    def append_rotated(self, k, v, frame0, n_frames, shots, tscale=None, shot_starts=None,
+                       f1=None):
+        """Rotate the keys of frames frame0 .. +n_frames-1 by their positions at
+        the window ending at f1 (default frame0 + n_frames), then append."""
+        f1 = frame0 + n_frames if f1 is None else f1
+        fss = [0] * n_frames if shot_starts is None else list(shot_starts)
+        pos = self.positions(range(frame0, frame0 + n_frames), f1, fss)
+        rows = np.repeat(pos, self.T)                               # per token
+        kk = np.asarray(k, np.float32).reshape(n_frames * self.T, self.H, self.D)
+        kr = rope.rotate_f32(kk, self.table[rows][:, None])         # same turn for all heads
+        return self.append(kr, v, frame0, n_frames, shots, tscale=tscale,
+                           shot_starts=shot_starts)
+
+    def rerotate(self, f1_from, f1_to):
+        """Move the stored key rotations from the window ending at f1_from to
+        the one ending at f1_to.  Returns the slots re-encoded."""
+        S, W = self.S, self.W
+        ws0, ws1 = ring.window_start(f1_from, S, W), ring.window_start(f1_to, S, W)
+        delta = ws1 - ws0
+        done = []
+        if delta == 0:
+            return done
+        for slot in range(S, S + W):
+            f = int(self.slot_frame[slot])
+            if not (ws1 <= f < f1_from):
+                continue
+            kh = nvfp4.decode_blocks(nvfp4.unpack_nibbles(self.k_codes[:, slot]),
+                                     self.k_scales[:, slot], self.k_tscale[slot])  # [H][Tc][D]
+            kr = rope.rotate_f32(kh, self.table[delta], inverse=True)
+            g = nvfp4.tensor_scale(kr)
+            codes, s8 = nvfp4.encode_blocks(kr, g)
+            self.k_codes[:, slot] = nvfp4.pack_nibbles(codes)
+            self.k_scales[:, slot] = s8
+            self.k_tscale[slot] = g
+            done.append(slot)
+        return done
