@@ -21,13 +21,15 @@ FP4KV_F32 = 0
 FP4KV_BF16 = 1
 FP4KV_FORMAT_NVFP4_V1 = 0x3146564E
 FP4KV_FORMAT_BF16_V1 = 0x36314642
+FP4KV_FORMAT_NVFP4_ROT_V1 = 0x3152564E
 FP4KV_MAX_FRAMES = 64
 FP4KV_MAX_WORKGROUPS = 4096
 FP4KV_MAX_SLOTS = 64
 
 EXPORTED = ("fp4kv_strerror", "fp4kv_abi_version", "fp4kv_cache_nbytes", "fp4kv_cache_reset",
             "fp4kv_append_workspace_bytes", "fp4kv_quantize_append", "fp4kv_rope_table",
-            "fp4kv_rope_rel", "fp4kv_attention_chunk", "fp4kv_attention_workspace_bytes")
+            "fp4kv_rope_rel", "fp4kv_attention_chunk", "fp4kv_attention_workspace_bytes",
+            "fp4kv_rerotate_window")
 
 
 class CacheDesc(ctypes.Structure):
@@ -89,6 +91,9 @@ def load() -> ctypes.CDLL:
                                           P(c_i32),
                                           vp, vp, ctypes.c_size_t, vp]
     lib.fp4kv_quantize_append.restype = c_int
+    lib.fp4kv_rerotate_window.argtypes = [P(CacheDesc), c_i32, c_i32, vp, c_i32, vp,
+                                          ctypes.c_size_t, vp]
+    lib.fp4kv_rerotate_window.restype = c_int
     lib.fp4kv_rope_table.argtypes = [P(c_f), c_i32, c_i32, ctypes.c_double]
     lib.fp4kv_rope_table.restype = c_int
     lib.fp4kv_rope_rel.argtypes = [vp, c_int, vp, c_int, c_i64, c_i32, c_i32, c_i32, c_i32,

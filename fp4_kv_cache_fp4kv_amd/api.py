@@ -47,24 +47,29 @@ class FP4KVCache:
 
     kv_format "nvfp4" (layout in include/fp4kv.h: codes uint8
     [H][S+W][Tc][D/2], scales uint8 [H][S+W][Tc][D/16], tensor scales float32
-    [S+W], slot metadata int32 [S+W]) or "bf16", the unquantized baseline
-    (keys bf16 [H][S+W][Tc][D], values bf16 [H][S+W][D][Tv], no scales).
+    [S+W], slot metadata int32 [S+W]), "nvfp4_rot" (the same layout with keys
+    stored already rotated; see rerotate_window) or "bf16", the unquantized
+    baseline (keys bf16 [H][S+W][Tc][D], values bf16 [H][S+W][D][Tv], no
+    scales).
     """
+
+    FORMATS = {"nvfp4": _lib.FP4KV_FORMAT_NVFP4_V1, "nvfp4_rot": _lib.FP4KV_FORMAT_NVFP4_ROT_V1,
+               "bf16": _lib.FP4KV_FORMAT_BF16_V1}
 
     def __init__(self, H: int, D: int, T: int, C: int, S: int, W: int,
                  token_stride: int = 1, rot_dim: Optional[int] = None,
                  device: str = "cuda:0", kv_format: str = "nvfp4",
                  sink_per_shot: bool = False):
         lib = load()
-        if kv_format not in ("nvfp4", "bf16"):
-            raise ValueError("kv_format must be 'nvfp4' or 'bf16'")
+        if kv_format not in self.FORMATS:
+            raise ValueError(f"kv_format must be one of {sorted(self.FORMATS)}")
         self.kv_format = kv_format
         self.device = torch.device(device)
         self.H, self.D, self.T, self.C, self.S, self.W = H, D, T, C, S, W
         self.token_stride = token_stride
         self.Tc = T // token_stride
         self.rot_dim = D if rot_dim is None else rot_dim
-        tag = _lib.FP4KV_FORMAT_NVFP4_V1 if kv_format == "nvfp4" else _lib.FP4KV_FORMAT_BF16_V1
+        tag = self.FORMATS[kv_format]
         self.desc = CacheDesc(format_tag=tag, n_heads=H, head_dim=D,
                               tokens_per_frame=T, token_stride=token_stride, chunk_frames=C,
                               sink_frames=S, window_frames=W, rot_dim=self.rot_dim,
@@ -149,6 +154,18 @@ def quantize_append(cache: FP4KVCache, k: torch.Tensor, v: torch.Tensor, frame0:
         _ptr(tscale), cache.workspace.data_ptr(), cache.workspace.numel(),
         _stream(cache.device))
     check(st, "fp4kv_quantize_append")
+
+
+def rerotate_window(cache: FP4KVCache, f1_from: int, f1_to: int) -> None:
+    """fp4kv_rerotate_window on the current stream: turn the surviving window
+    keys of an "nvfp4_rot" cache from the window ending at f1_from to the one
+    ending at f1_to (call it before the append that moves the window)."""
+    if cache.kv_format != "nvfp4_rot":
+        raise ValueError("rerotate_window needs a cache with kv_format 'nvfp4_rot'")
+    st = load().fp4kv_rerotate_window(
+        ctypes.byref(cache.desc), int(f1_from), int(f1_to), cache.cos_sin.data_ptr(), cache.n_pos,
+        cache.workspace.data_ptr(), cache.workspace.numel(), _stream(cache.device))
+    check(st, "fp4kv_rerotate_window")
 
 
 def rope_rel(x: torch.Tensor, pos0: int, tokens_per_frame: int, cos_sin: torch.Tensor,

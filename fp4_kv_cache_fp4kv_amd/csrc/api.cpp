@@ -14,7 +14,7 @@ using namespace fp4kv;
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -27,7 +27,8 @@ int padded_tokens(const fp4kv_cache *c) {
 // Shape checks of a cache descriptor (no pointer reads).
 int check_shape(const fp4kv_cache *c) {
   if (!c) return FP4KV_EINVAL;
-  if (c->format_tag != FP4KV_FORMAT_NVFP4_V1 && c->format_tag != FP4KV_FORMAT_BF16_V1)
+  if (c->format_tag != FP4KV_FORMAT_NVFP4_V1 && c->format_tag != FP4KV_FORMAT_BF16_V1 &&
+      c->format_tag != FP4KV_FORMAT_NVFP4_ROT_V1)
     return FP4KV_EFORMAT;
   if (c->n_heads < 1 || c->tokens_per_frame < 1 || c->chunk_frames < 1 || c->sink_frames < 0)
     return FP4KV_EINVAL;
@@ -45,6 +46,13 @@ int check_shape(const fp4kv_cache *c) {
 }
 
 bool is_bf16(const fp4kv_cache *c) { return c->format_tag == FP4KV_FORMAT_BF16_V1; }
+
+// Keys stored already rotated by their cache-relative position.
+bool keys_rotated(const fp4kv_cache *c) { return c->format_tag == FP4KV_FORMAT_NVFP4_ROT_V1; }
+
+int window_start(const fp4kv_cache *c, long long f1) {
+  return (int)std::max<long long>(c->sink_frames, f1 - c->window_frames);
+}
 
 int check_buffers(const fp4kv_cache *c) {
   const void *ptrs[] = {c->k_codes, c->v_codes, c->k_tscale, c->v_tscale,
@@ -176,6 +184,45 @@ int fp4kv_quantize_append(const fp4kv_cache *c, const void *k, const void *v, in
   return from_hip(launch_append(p, (hipStream_t)stream));
 }
 
+int fp4kv_rerotate_window(const fp4kv_cache *c, int32_t f1_from, int32_t f1_to,
+                          const float *cos_sin, int32_t n_pos, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  int st = check_shape(c);
+  if (st) return st;
+  if ((st = check_buffers(c))) return st;
+  if (!keys_rotated(c)) return FP4KV_EINVAL;
+  if (f1_from < 0 || f1_to < f1_from || f1_to > (1 << 30) || !workspace) return FP4KV_EINVAL;
+  if (c->rot_dim > 0 && !cos_sin) return FP4KV_EINVAL;
+  if (workspace_bytes < kWsBytes) return FP4KV_ESHAPE;
+  if (!aligned16(workspace) || ((uintptr_t)cos_sin & 7u)) return FP4KV_EALIGN;
+  const int ws0 = window_start(c, f1_from), ws1 = window_start(c, f1_to);
+  const int delta = ws1 - ws0;
+  if (delta == 0 || ws1 >= f1_from) return FP4KV_OK;   // nothing survives a move
+  if (c->rot_dim > 0 && delta >= n_pos) return FP4KV_ESHAPE;
+  const long long units = (long long)c->n_heads * (c->tokens_per_frame / c->token_stride) *
+                          (c->head_dim / 16);   // (key row, block) pairs of one slot
+  if (units >= (1ll << 31)) return FP4KV_ESHAPE;
+
+  RerotParams p;
+  memset(&p, 0, sizeof(p));
+  p.codes = c->k_codes;
+  p.scales = c->k_scales;
+  p.tscale = c->k_tscale;
+  p.slot_frame = c->slot_frame;
+  p.cs = c->rot_dim > 0 ? cos_sin + (size_t)delta * c->rot_dim : nullptr;
+  p.ws_max = (uint32_t *)workspace;
+  p.ws_g = (float *)((uint32_t *)workspace + (size_t)FP4KV_MAX_SLOTS * kRotParts);
+  p.H = c->n_heads;
+  p.D = c->head_dim;
+  p.Tc = c->tokens_per_frame / c->token_stride;
+  p.S = c->sink_frames;
+  p.n_slots = c->sink_frames + c->window_frames;
+  p.half_rot = c->rot_dim / 2;
+  p.f_lo = ws1;
+  p.f_hi = f1_from;
+  return from_hip(launch_rerotate(p, c->window_frames, (hipStream_t)stream));
+}
+
 int fp4kv_rope_table(float *cos_sin, int32_t n_pos, int32_t rot_dim, double base) {
   if (!cos_sin || n_pos < 1 || rot_dim < 2 || (rot_dim & 1) || !(base > 1.0)) return FP4KV_EINVAL;
   const int half = rot_dim / 2;
@@ -192,7 +239,7 @@ int fp4kv_rope_table(float *cos_sin, int32_t n_pos, int32_t rot_dim, double base
 int fp4kv_rope_rel(const void *x, int in_dtype, void *y, int out_dtype, int64_t n_tokens,
                    int32_t n_heads, int32_t head_dim, int32_t tokens_per_frame, int32_t pos0,
                    int32_t rot_dim, const float *cos_sin, int32_t n_pos, void *stream) {
-  if (!x || !y || !cos_sin) return FP4KV_EINVAL;
+  if (!x || !y || (!cos_sin && rot_dim > 0)) return FP4KV_EINVAL;
   if (in_dtype != FP4KV_F32 && in_dtype != FP4KV_BF16) return FP4KV_EINVAL;
   if (out_dtype != FP4KV_F32 && out_dtype != FP4KV_BF16) return FP4KV_EINVAL;
   if (n_tokens < 0 || n_heads < 1 || tokens_per_frame < 1 || pos0 < 0 || n_pos < 1)
@@ -202,7 +249,8 @@ int fp4kv_rope_rel(const void *x, int in_dtype, void *y, int out_dtype, int64_t 
   if (!aligned16(x) || !aligned16(y) || ((uintptr_t)cos_sin & 7u)) return FP4KV_EALIGN;
   if (x == y && in_dtype != out_dtype) return FP4KV_EINVAL;
   if (n_tokens == 0) return FP4KV_OK;
-  if ((long long)pos0 + (n_tokens - 1) / tokens_per_frame >= n_pos) return FP4KV_ESHAPE;
+  if (rot_dim > 0 && (long long)pos0 + (n_tokens - 1) / tokens_per_frame >= n_pos)
+    return FP4KV_ESHAPE;   // rot_dim 0 reads no table
   if (n_tokens * n_heads * (long long)head_dim > (1ll << 40)) return FP4KV_ESHAPE;
   RopeParams p;
   p.x = x;
@@ -227,13 +275,14 @@ int fp4kv_attention_chunk(const fp4kv_cache *c, const void *q_rot, int q_dtype, 
   int st = check_shape(c);
   if (st) return st;
   if ((st = check_buffers(c))) return st;
-  if (!q_rot || !o || !q_shot || !cos_sin) return FP4KV_EINVAL;
+  const bool rotated = keys_rotated(c);   // no key rotation, no table
+  if (!q_rot || !o || !q_shot || (!cos_sin && !rotated)) return FP4KV_EINVAL;
   if (out_dtype != FP4KV_F32 && out_dtype != FP4KV_BF16) return FP4KV_EINVAL;
   if (q_dtype != FP4KV_F32 && q_dtype != FP4KV_BF16) return FP4KV_EINVAL;
   if (q_frame0 < 0 || n_q_frames < 1 || n_q_frames > FP4KV_MAX_FRAMES) return FP4KV_EINVAL;
   if ((long long)q_frame0 + n_q_frames > (1ll << 30)) return FP4KV_EINVAL;
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return FP4KV_EINVAL;
-  if (n_pos < c->sink_frames + c->window_frames) return FP4KV_ESHAPE;
+  if (!rotated && n_pos < c->sink_frames + c->window_frames) return FP4KV_ESHAPE;
   if (!aligned16(q_rot) || !aligned16(o) || ((uintptr_t)cos_sin & 7u)) return FP4KV_EALIGN;
   if (q_rot == o) return FP4KV_EINVAL;
   const long long nq = (long long)n_q_frames * c->tokens_per_frame;
@@ -262,7 +311,7 @@ int fp4kv_attention_chunk(const fp4kv_cache *c, const void *q_rot, int q_dtype, 
   p.S = c->sink_frames;
   p.W = c->window_frames;
   p.n_slots = c->sink_frames + c->window_frames;
-  p.rot_dim = c->rot_dim;
+  p.rot_dim = rotated ? 0 : c->rot_dim;   // rot_dim 0: the kernel turns nothing
   p.q_frame0 = q_frame0;
   p.n_q_frames = n_q_frames;
   p.Nq = (int)nq;

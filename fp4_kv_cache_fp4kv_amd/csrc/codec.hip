@@ -8,7 +8,8 @@
 //   encode_kernel  NVFP4 encode of both tensors straight into their cache
 //                  slots (layouts in include/fp4kv.h), plus the slot metadata.
 // The bf16 baseline format takes one kernel (store_bf16_kernel): a copy into
-// the same ring layout.
+// the same ring layout.  Caches that store keys rotated also take the window
+// re-rotation below (rerot_amax_kernel, rerot_encode_kernel).
 #include "fp4kv_device.hpp"
 #include "internal.hpp"
 
@@ -335,6 +336,102 @@ __global__ __launch_bounds__(kThreads) void store_bf16_kernel(AppendParams p) {
   }
 }
 
+// ---- window re-rotation (keys stored rotated, FP4KV_FORMAT_NVFP4_ROT_V1) ----
+//
+// When the window start moves by delta, every surviving window key is turned
+// by -delta in place: decode, rotate in float32, re-encode with a fresh
+// tensor scale over the slot (all heads).  Two kernels, grid.y = window slot:
+//   rerot_amax_kernel    grid (kRotParts, W): partial max |turned key| per
+//                        workgroup of a slot, plus the slot's old scale;
+//   rerot_encode_kernel  one thread per (key row, 16-block): decode, turn,
+//                        encode in place with g = amax / 2688.
+// A workgroup whose slot holds no frame to turn returns at once.
+
+__device__ __forceinline__ bool rerot_slot(const RerotParams &p, int s) {
+  const int f = p.slot_frame[s];
+  return f >= p.f_lo && f < p.f_hi;
+}
+
+// Key block b of a row: decode x = sign * fl(fl(E2M1 * E4M3) * g), then turn
+// pair (2e, 2e+1), rotary pair 8b + e, by -delta with the exact float32
+// arithmetic; pairs past rot_dim / 2 are kept.
+__device__ __forceinline__ void decode_turn(const RerotParams &p, uint2 w, uint32_t s8, float g,
+                                            int b, float (&x)[16]) {
+  const float sv = e4m3_value(s8);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t nib = ((i < 8 ? w.x : w.y) >> (4 * (i & 7))) & 0xFu;
+    const float v = (e2m1_value(nib & 7u) * sv) * g;
+    x[i] = (nib & 8u) ? -v : v;
+  }
+  const float2 *cs = (const float2 *)p.cs;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int pair = 8 * b + e;
+    if (pair < p.half_rot) {
+      const float2 t = cs[pair];
+      float ra, rb;
+      rotate_pair_exact(x[2 * e], x[2 * e + 1], t.x, -t.y, ra, rb);
+      x[2 * e] = ra;
+      x[2 * e + 1] = rb;
+    }
+  }
+}
+
+__device__ __forceinline__ long long rerot_row(const RerotParams &p, int s, uint32_t r) {
+  const int h = (int)(r / (uint32_t)p.Tc), tc = (int)(r - (uint32_t)h * (uint32_t)p.Tc);
+  return ((long long)h * p.n_slots + s) * p.Tc + tc;
+}
+
+__global__ __launch_bounds__(kThreads) void rerot_amax_kernel(RerotParams p) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int s = p.S + (int)blockIdx.y;
+  if (!rerot_slot(p, s)) return;
+  const float g = p.tscale[s];
+  const int nb = p.D >> 4;
+  const uint32_t units = (uint32_t)(p.H * p.Tc * nb);
+  uint32_t m = 0;
+  for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < units; u += gridDim.x * kThreads) {
+    const int b = (int)(u % (uint32_t)nb);
+    const long long row = rerot_row(p, s, u / (uint32_t)nb);
+    const uint2 w = *(const uint2 *)(p.codes + row * (p.D >> 1) + b * 8);
+    float x[16];
+    decode_turn(p, w, p.scales[row * nb + b], g, b, x);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+  }
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) {
+    p.ws_max[s * kRotParts + blockIdx.x] = m;
+    if (blockIdx.x == 0) p.ws_g[s] = g;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void rerot_encode_kernel(RerotParams p) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int s = p.S + (int)blockIdx.y;
+  if (!rerot_slot(p, s)) return;
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < kRotParts; i += kThreads) m = max(m, p.ws_max[s * kRotParts + i]);
+  m = block_max_u32(m, red);
+  const float amax = __uint_as_float(m);
+  const float g = amax > 0.0f ? __fdiv_rn(amax, 2688.0f) : 1.0f;
+  const float d = 6.0f * g;
+  if (blockIdx.x == 0 && threadIdx.x == 0) p.tscale[s] = g;
+  const int nb = p.D >> 4;
+  const uint32_t units = (uint32_t)(p.H * p.Tc * nb);
+  const uint32_t u = blockIdx.x * kThreads + threadIdx.x;
+  if (u >= units) return;
+  const int b = (int)(u % (uint32_t)nb);
+  const long long row = rerot_row(p, s, u / (uint32_t)nb);
+  uint2 *cp = (uint2 *)(p.codes + row * (p.D >> 1) + b * 8);
+  float x[16];
+  decode_turn(p, *cp, p.scales[row * nb + b], p.ws_g[s], b, x);
+  uint32_t s8;
+  *cp = encode_block(x, g, d, &s8);
+  p.scales[row * nb + b] = (uint8_t)s8;
+}
+
 __global__ void reset_kernel(int32_t *slot_frame, int32_t *slot_shot, float *kt, float *vt, int n) {
   const int i = threadIdx.x;
   if (i < n) {
@@ -376,6 +473,16 @@ hipError_t launch_append(const AppendParams &p_in, hipStream_t s) {
   }
   hipLaunchKernelGGL(encode_kernel, dim3((unsigned)(p.v_blocks + k_blocks)), dim3(kThreads), 0, s,
                      p);
+  return hipGetLastError();
+}
+
+hipError_t launch_rerotate(const RerotParams &p, int window_slots, hipStream_t s) {
+  const long long units = (long long)p.H * p.Tc * (p.D >> 4);
+  hipLaunchKernelGGL(rerot_amax_kernel, dim3(kRotParts, window_slots), dim3(kThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned blocks = (unsigned)((units + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(rerot_encode_kernel, dim3(blocks, window_slots), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

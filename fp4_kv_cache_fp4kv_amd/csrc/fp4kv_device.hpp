@@ -79,4 +79,14 @@ __device__ __forceinline__ void rotate_pair(float a, float b, float c, float s,
   rb = a * s + b * c;
 }
 
+// The same turn with every product rounded to float32 before the sum is
+// rounded (no fused multiply-add): the arithmetic of rotations whose result
+// is stored or NVFP4-encoded, so that it can be reproduced exactly.
+__device__ __forceinline__ void rotate_pair_exact(float a, float b, float c, float s,
+                                                  float &ra, float &rb) {
+#pragma clang fp contract(off)
+  ra = a * c - b * s;
+  rb = a * s + b * c;
+}
+
 }  // namespace fp4kv

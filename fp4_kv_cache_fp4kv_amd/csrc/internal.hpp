@@ -11,9 +11,16 @@ namespace fp4kv {
 // Number of partial maxima per tensor in the append workspace.
 constexpr int kAmaxBlocks = 256;
 
+// Partial maxima per cache slot in the re-rotation's amax pass.
+constexpr int kRotParts = 32;
+
 // Workspace of fp4kv_quantize_append: uint32 partial maxima [2][kAmaxBlocks]
-// (float32 bit patterns of max |x| per workgroup of the amax pass).
-constexpr size_t kWsBytes = 2 * kAmaxBlocks * sizeof(uint32_t);
+// (float32 bit patterns of max |x| per workgroup of the amax pass).  The
+// window re-rotation uses the same workspace: partial maxima
+// [FP4KV_MAX_SLOTS][kRotParts], then the old tensor scales [FP4KV_MAX_SLOTS].
+constexpr size_t kAppendWsBytes = 2 * kAmaxBlocks * sizeof(uint32_t);
+constexpr size_t kRotWsBytes = (size_t)FP4KV_MAX_SLOTS * (kRotParts + 1) * sizeof(uint32_t);
+constexpr size_t kWsBytes = kAppendWsBytes > kRotWsBytes ? kAppendWsBytes : kRotWsBytes;
 
 struct AppendParams {
   const void *x[2];        // K, V inputs [n_frames*T][H][D]
@@ -29,6 +36,18 @@ struct AppendParams {
   int v_blocks;            // workgroups of the value pass in encode_kernel
   int32_t shot[FP4KV_MAX_FRAMES];
   int32_t slot[FP4KV_MAX_FRAMES];   // cache slot of each frame (host-computed)
+};
+
+// Window re-rotation of keys stored rotated (FP4KV_FORMAT_NVFP4_ROT_V1).
+struct RerotParams {
+  uint8_t *codes, *scales;   // key codes and block scales
+  float *tscale;             // key tensor scales [n_slots]
+  const int32_t *slot_frame;
+  const float *cs;           // table row delta: (cos, sin) per rotary pair
+  uint32_t *ws_max;          // [n_slots][kRotParts] partial maxima
+  float *ws_g;               // [n_slots] tensor scales before the call
+  int H, D, Tc, S, n_slots, half_rot;
+  int f_lo, f_hi;            // window frames f_lo <= f < f_hi are turned
 };
 
 struct RopeParams {
@@ -60,6 +79,7 @@ struct AttnParams {
 
 hipError_t launch_cache_reset(const fp4kv_cache &c, hipStream_t s);
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
+hipError_t launch_rerotate(const RerotParams &p, int window_slots, hipStream_t s);
 hipError_t launch_rope(const RopeParams &p, hipStream_t s);
 hipError_t launch_attention(const AttnParams &p, int head_dim, int out_f32, hipStream_t s);
 

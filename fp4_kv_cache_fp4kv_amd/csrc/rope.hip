@@ -5,7 +5,9 @@
 //
 // One thread per 8 consecutive elements of one (token, head) row: four rotary
 // pairs and 32 bytes of table.  Memory-bound: 2 or 4 bytes read and 2 or 4
-// written per element.
+// written per element.  Products are rounded before the sum (no fused
+// multiply-add), so keys rotated here before they are stored encode to the
+// same codes wherever the rotation is reproduced.
 #include "fp4kv_device.hpp"
 #include "internal.hpp"
 
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeParams p) {
       r[2 * i + 1] = x[2 * i + 1];
       if (pair < half) {
         const float2 cs = *(const float2 *)(tab + 2 * pair);
-        rotate_pair(x[2 * i], x[2 * i + 1], cs.x, cs.y, r[2 * i], r[2 * i + 1]);
+        rotate_pair_exact(x[2 * i], x[2 * i + 1], cs.x, cs.y, r[2 * i], r[2 * i + 1]);
       }
     }
     if (p.out_f32) {

@@ -60,6 +60,8 @@ extern "C" {
 #define FP4KV_FORMAT_NVFP4_V1 0x3146564Eu
 /* Baseline format: keys and values kept as bf16 (see fp4kv_cache). */
 #define FP4KV_FORMAT_BF16_V1  0x36314642u
+/* NVFP4 layout with keys stored after rotation (see fp4kv_cache). */
+#define FP4KV_FORMAT_NVFP4_ROT_V1 0x3152564Eu
 
 /* Limits.  Frames per call and cache slots are passed to kernels by value. */
 #define FP4KV_MAX_FRAMES 64   /* frames per append or attention call      */
@@ -89,6 +91,17 @@ extern "C" {
  * Keys are stored BEFORE rotary rotation; attention rotates them by their
  * cache-relative position at every step, so stored codes never change when
  * the window slides.
+ *
+ * Rotate-at-write format FP4KV_FORMAT_NVFP4_ROT_V1 (the other reading of
+ * KV-cache relative RoPE; refft.com, question "How do KV-cache relative
+ * RoPE and TriAttention work together ..."): the same buffers and layout,
+ * but k_codes hold keys ALREADY rotated by their cache-relative position
+ * (pos(f) below, for the window that ends after the append).  The caller
+ * rotates new keys with fp4kv_rope_rel (float32 output) before
+ * fp4kv_quantize_append, and calls fp4kv_rerotate_window before each append
+ * that moves the window start, which turns the surviving window keys in
+ * place.  Attention then uses keys as stored.  Each window key is
+ * re-encoded once per step it survives, which adds rounding error.
  *
  * NVFP4 blocks are 16 consecutive elements along D for keys and values.
  * Keys are stored token-major; values are stored dimension-major so that the
@@ -205,6 +218,34 @@ int fp4kv_quantize_append(const fp4kv_cache *c, const void *k, const void *v,
                           void *stream);
 
 /*
+ * fp4kv_rerotate_window - move the stored key rotations of a
+ * FP4KV_FORMAT_NVFP4_ROT_V1 cache from the window ending at frame f1_from
+ * to the one ending at f1_to (KV-cache relative RoPE, rotate-at-write
+ * reading; refft.com, question "How do KV-cache relative RoPE and
+ * TriAttention work together ...").
+ *
+ * With ws(f1) = max(S, f1 - W) and delta = ws(f1_to) - ws(f1_from), every
+ * window slot (slot >= S) whose frame f has ws(f1_to) <= f < f1_from is
+ * turned by -delta: each key element is decoded as
+ * sign * fl(fl(E2M1 * E4M3) * g), pair (2i, 2i+1), i < rot_dim/2, becomes
+ * (fl(fl(a c) + fl(b s)), fl(fl(b c) - fl(a s))) with (c, s) = cos_sin[delta][i]
+ * (float32, no fused multiply-add), and the slot's keys are encoded again
+ * as in fp4kv_quantize_append with a new tensor scale amax / 2688 over the
+ * slot (all heads).  Sink slots, values and slot metadata are untouched.
+ * Nothing is enqueued when delta = 0 or no window frame survives.
+ *   f1_from     0 <= f1_from <= f1_to: the window end the stored rotations
+ *               belong to (the end of the previous append).
+ *   cos_sin     device table from fp4kv_rope_table (cache->rot_dim) with
+ *               n_pos > delta rows; may be NULL when rot_dim = 0.
+ *   workspace   device, fp4kv_append_workspace_bytes() bytes, 16-byte
+ *               aligned (partial maxima between the call's two kernels).
+ * Errors: FP4KV_EINVAL for a cache of another format.
+ */
+int fp4kv_rerotate_window(const fp4kv_cache *c, int32_t f1_from, int32_t f1_to,
+                          const float *cos_sin, int32_t n_pos, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
  * fp4kv_rope_table - fill a rotary table on the host (no GPU):
  *   cos_sin[p][i][0] = cos(p * base^(-2i/rot_dim)),
  *   cos_sin[p][i][1] = sin(p * base^(-2i/rot_dim)),
@@ -222,13 +263,15 @@ int fp4kv_rope_table(float *cos_sin, int32_t n_pos, int32_t rot_dim, double base
  *
  * Token t belongs to frame t / T and is rotated by position pos0 + t / T:
  * each pair (2i, 2i+1), i < rot_dim/2, turns by cos_sin[pos][i], i.e.
- * (a, b) -> (a c - b s, a s + b c).  Dimensions past rot_dim are copied.
- * Math in float32; a bf16 output is rounded to nearest even.
+ * (a, b) -> (fl(fl(a c) - fl(b s)), fl(fl(a s) + fl(b c))): float32, each
+ * product rounded before the sum, no fused multiply-add.  Dimensions past
+ * rot_dim are copied.  A bf16 output is rounded to nearest even.
  *   x         device, in_dtype (FP4KV_F32 or FP4KV_BF16), 16-byte aligned.
  *   y         device, out_dtype (FP4KV_F32 or FP4KV_BF16), same shape; may
  *             alias x when in_dtype == out_dtype.
  *   cos_sin   device table from fp4kv_rope_table with n_pos rows;
- *             pos0 + (n_tokens - 1) / T must be < n_pos.
+ *             pos0 + (n_tokens - 1) / T must be < n_pos.  With rot_dim = 0
+ *             (a copy) the table is not read and may be NULL.
  * The attention kernel takes float32 rotated queries (bf16 is accepted but
  * rounds the queries once more).
  */
@@ -251,8 +294,9 @@ int fp4kv_rope_rel(const void *x, int in_dtype, void *y, int out_dtype, int64_t 
  * the sink and window follow heatdrop.ai, section "What it does".
  * Cache-relative position: pos(f) = f if f < S else S + (f - ws), for keys
  * and queries alike.  Scores are softmax_scale * (R(pos(qf)) q) . (R(pos(kf)) k)
- * with k the decoded (pre-rotation) key; the output of a query row is the
- * softmax-weighted sum of the decoded values.
+ * with k the decoded (pre-rotation) key; for FP4KV_FORMAT_NVFP4_ROT_V1 the
+ * stored key is already R(pos(kf)) k and is used as decoded.  The output of
+ * a query row is the softmax-weighted sum of the decoded values.
  *
  * Arithmetic: MFMA with f16 operands and float32 accumulation.  Decoded keys
  * and values are exact in f16 (tensor scales are applied in float32); the
@@ -267,7 +311,8 @@ int fp4kv_rope_rel(const void *x, int in_dtype, void *y, int out_dtype, int64_t 
  *           FP4KV_BF16), 16-byte aligned, must not alias q_rot.
  *   q_shot  host [n_q_frames]: shot id of each query frame.
  *   cos_sin device rotary table with n_pos >= S + W rows (fp4kv_rope_table,
- *           cache->rot_dim).
+ *           cache->rot_dim); not read for FP4KV_FORMAT_NVFP4_ROT_V1 (keys
+ *           are stored rotated), where it may be NULL.
  * Rows with no visible key are written as zeros.
  *
  * Work split: the key tiles of all (256-row block, head) pairs are cut into

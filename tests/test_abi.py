@@ -58,10 +58,10 @@ def _desc(**kw):
 
 def test_strerror_and_version():
     lib = _lib.load()
-    assert lib.fp4kv_abi_version() == 2
+    assert lib.fp4kv_abi_version() == 3
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.fp4kv_strerror(st)
-    assert lib.fp4kv_append_workspace_bytes() >= 64
+    assert lib.fp4kv_append_workspace_bytes() >= 64 * 33 * 4   # re-rotation maxima
 
 
 def test_attention_workspace_bytes():
@@ -116,6 +116,42 @@ def test_bf16_format_sizes():
     assert list(out) == [H * n * Tc * D * 2, H * n * D * Tv * 2, 0, 0, n * 4, n * 4]
     c = _desc(format_tag=0x12345678)
     assert lib.fp4kv_cache_nbytes(ctypes.byref(c), out) == _lib.FP4KV_EFORMAT
+
+
+def test_rotated_format_has_the_nvfp4_sizes():
+    lib = _lib.load()
+    a, b = (ctypes.c_size_t * 6)(), (ctypes.c_size_t * 6)()
+    assert lib.fp4kv_cache_nbytes(ctypes.byref(_desc()), a) == 0
+    c = _desc(format_tag=_lib.FP4KV_FORMAT_NVFP4_ROT_V1)
+    assert lib.fp4kv_cache_nbytes(ctypes.byref(c), b) == 0
+    assert list(a) == list(b)
+
+
+def test_rerotate_validation_before_launch():
+    lib = _lib.load()
+    c = _desc(format_tag=_lib.FP4KV_FORMAT_NVFP4_ROT_V1)     # S = 3, W = 12, C = 3
+    A, Wk = 0x100000, 0x4000000
+    ws = lib.fp4kv_append_workspace_bytes()
+    call = lambda **kw: lib.fp4kv_rerotate_window(
+        ctypes.byref(kw.get("c", c)), kw.get("f0", 15), kw.get("f1", 18), kw.get("cs", A),
+        kw.get("npos", 15), kw.get("ws", Wk), kw.get("wsb", ws), None)
+    assert call(c=_desc()) == -1                     # keys stored before rotation
+    assert call(c=_desc(format_tag=_lib.FP4KV_FORMAT_BF16_V1)) == -1
+    assert call(c=_desc(format_tag=7)) == -4
+    assert call(f0=-1) == -1
+    assert call(f0=18, f1=15) == -1                  # the window only moves forward
+    assert call(ws=None) == -1
+    assert call(cs=None) == -1
+    assert call(wsb=ws - 1) == -2
+    assert call(ws=Wk + 8) == -3
+    assert call(cs=A + 4) == -3
+    assert call(npos=3) == -2                        # delta 3 needs table row 3
+    # nothing to move: window not full yet, no move, or nothing survives
+    assert call(f0=6, f1=9) == 0
+    assert call(f0=18, f1=18) == 0
+    assert call(f0=15, f1=30) == 0
+    r0 = _desc(format_tag=_lib.FP4KV_FORMAT_NVFP4_ROT_V1, rot_dim=0)
+    assert call(c=r0, f0=6, f1=9, cs=None) == 0       # rot_dim 0 needs no table
 
 
 def test_stride_must_divide_tokens():
@@ -173,6 +209,9 @@ def test_rope_validation_before_launch():
     assert call(dt=0) == -1            # in place needs matching dtypes
     assert call(odt=3) == -1
     assert call(n=0) == 0              # nothing to do, nothing launched
+    assert call(cs=None) == -1
+    assert call(rd=0, cs=None, n=0) == 0   # rot_dim 0 reads no table
+    assert call(rd=0, pos0=40, n=0) == 0
 
 
 def test_attention_validation_before_launch():
@@ -203,6 +242,9 @@ def test_attention_validation_before_launch():
     assert call(dt=5) == -1
     assert call(qdt=2) == -1
     assert call(c=_desc(format_tag=1)) == -4
+    assert call(cs=None) == -1                       # keys stored before rotation need it
+    rot = _desc(format_tag=_lib.FP4KV_FORMAT_NVFP4_ROT_V1)
+    assert call(c=rot, cs=None, npos=0, n=0) == -1   # validation still runs
 
 
 def test_rope_table_host_values():
@@ -215,3 +257,15 @@ def test_rope_table_host_values():
             assert abs(buf[(p * 4 + i) * 2] - math.cos(ang)) < 1e-7
             assert abs(buf[(p * 4 + i) * 2 + 1] - math.sin(ang)) < 1e-7
     assert _lib.load().fp4kv_rope_table(buf, 6, 7, 10000.0) == -1
+
+
+def test_rope_table_matches_the_oracle_table_bit_for_bit():
+    # keys stored rotated are encoded from rotations by this table, so the
+    # library's host table and the oracle's must agree exactly
+    import numpy as np
+    from oracle import rope
+    for n_pos, rd in ((15, 128), (8, 64), (21, 96)):
+        buf = (ctypes.c_float * (n_pos * rd))()
+        assert _lib.load().fp4kv_rope_table(buf, n_pos, rd, 10000.0) == 0
+        lib_t = np.frombuffer(bytearray(buf), dtype=np.float32).reshape(n_pos, rd // 2, 2)
+        assert np.array_equal(lib_t.view(np.uint32), rope.table_f32(n_pos, rd).view(np.uint32))
