@@ -12,11 +12,17 @@ bf16 inputs ~N(0,1) with 1% outliers x20.  --workload picks another.
 
 Printed: one JSON line.  value = frames/s of one layer = C * K / time of K
 steps.  roofline = the attention kernel (the dominant one): algorithmic
-FLOP per launch 4*H*Nq*Nk*D / its mean duration from HIP events on the
-launch stream, against the 2.5 PFLOP/s dense f16/bf16 MFMA peak.
-roofline_codec = the two append kernels: algorithmic bytes (kept K and V
-read once, codes and scales written once) / their mean duration, against
-8 TB/s.  cpu_baseline = the CPU oracle on a bounded sample of the same step.
+FLOP per launch (4*D per (query, key) pair the masks keep) / its mean
+duration from HIP events on the launch stream, against the 2.5 PFLOP/s
+dense f16/bf16 MFMA peak.  roofline_codec = the two append kernels:
+algorithmic bytes (kept K and V read once, codes and scales written once)
+/ their mean duration, against 8 TB/s.  cpu_baseline = the CPU oracle on a
+bounded sample of the same step.
+
+--kv nvfp4_rot stores keys rotated; the step becomes
+    fp4kv_quantize_append_rotated(K, V) -> fp4kv_rope_rel(Q) -> fp4kv_attention_chunk
+and roofline_codec covers the first (the cache update: the append plus the
+re-encoding of the window keys that survive the window move).
 """
 from __future__ import annotations
 
@@ -40,8 +46,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="l13b")
-    ap.add_argument("--kv", default="nvfp4", choices=("nvfp4", "bf16"),
-                    help="cache format: NVFP4 (the path) or the bf16 baseline")
+    ap.add_argument("--kv", default="nvfp4", choices=("nvfp4", "nvfp4_rot", "bf16"),
+                    help="cache format: NVFP4 with keys stored before rotation (the path), "
+                         "NVFP4 with keys stored rotated (re-rotated when the window "
+                         "moves), or the bf16 baseline")
     ap.add_argument("--sink-per-shot", action="store_true",
                     help="per-shot attention sinks (each shot re-anchors the sink)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -141,6 +149,17 @@ def visible_pairs(w, f0, per_shot, shot_start):
     return n
 
 
+def surviving_window_frames(w, f0, per_shot, shot_start):
+    """Window frames whose stored rotation moves at the chunk step starting at
+    frame f0 (keys stored rotated): frames in window slots that stay in the
+    window while its start moves."""
+    ws0, ws1 = max(w.S, f0 - w.W), max(w.S, f0 + w.C - w.W)
+    if ws1 == ws0:
+        return 0
+    return sum(1 for f in range(ws1, f0)
+               if not (per_shot and f - shot_start(f) < w.S))
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -180,6 +199,7 @@ def main():
         sets.append(tuple(dev_t(*wl.draw(w, c, tid, n_tokens=n_tok))
                           for tid in (wl.Q_ID, wl.K_ID, wl.V_ID)))
     qrot = torch.empty((w.C * w.T, w.H, w.D), dtype=torch.float32, device=dev)
+    rot = args.kv == "nvfp4_rot"
     out = torch.empty((w.C * w.T, w.H, w.D), dtype=torch.bfloat16, device=dev)
     first = -(-(w.S + w.W) // w.C)       # first chunk step with a full window
 
@@ -190,19 +210,25 @@ def main():
         f0 = c * w.C
         shots = [w.shot_of(f) for f in range(f0, f0 + w.C)]
         fss = [shot_start(f) for f in range(f0, f0 + w.C)] if args.sink_per_shot else None
+        def rope(x, y):
+            if fss is None:
+                api.rope_rel(x, api.cache_positions(w.S, w.W, f0, w.C), w.T, gc.cos_sin, out=y)
+            else:   # per-frame positions (a cut inside the chunk breaks the sequence)
+                for j in range(w.C):
+                    rows = slice(j * w.T, (j + 1) * w.T)
+                    api.rope_rel(x[rows], api.frame_position(w.S, w.W, f0 + j, f0 + w.C, fss[j]),
+                                 w.T, gc.cos_sin, out=y[rows])
+
         if record:
             e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             e[0].record()
-        api.quantize_append(gc, k, v, f0, w.C, shots, shot_starts=fss)
+        if rot:   # turn the surviving window keys, store the new keys rotated
+            api.quantize_append_rotated(gc, k, v, f0, w.C, shots, shot_starts=fss)
+        else:
+            api.quantize_append(gc, k, v, f0, w.C, shots, shot_starts=fss)
         if record:
             e[1].record()
-        if fss is None:
-            api.rope_rel(q, api.cache_positions(w.S, w.W, f0, w.C), w.T, gc.cos_sin, out=qrot)
-        else:   # per-frame positions (a cut inside the chunk breaks the sequence)
-            for j in range(w.C):
-                rows = slice(j * w.T, (j + 1) * w.T)
-                api.rope_rel(q[rows], api.frame_position(w.S, w.W, f0 + j, f0 + w.C, fss[j]),
-                             w.T, gc.cos_sin, out=qrot[rows])
+        rope(q, qrot)
         if record:
             e[2].record()
         api.attention_chunk(gc, qrot, f0, w.C, shots, out=out)
@@ -242,6 +268,13 @@ def main():
     es = 2 if w.dtype == "bf16" else 4
     kept = 2 * w.C * w.Tc * w.H * w.D
     codec_bytes = kept * es + kept * (2.0 if args.kv == "bf16" else 0.5 + 1.0 / 16.0)
+    if rot:
+        # cache update: the append plus the re-encoding of the surviving
+        # window keys (their codes and scales read and written once)
+        surv = [surviving_window_frames(w, (c - args.steps + i) * w.C, args.sink_per_shot,
+                                        shot_start) for i in range(args.steps)]
+        key_frame = w.H * w.Tc * (w.D // 2 + w.D // 16)
+        codec_bytes += 2.0 * key_frame * sum(surv) / len(surv)
     codec_gbs = codec_bytes / (codec_ms * 1e-3) / 1e9
 
     # HBM bytes per attention launch from rocprofv3 counters, valid only for
@@ -274,7 +307,7 @@ def main():
                    "frames_per_step": w.C, "attention_ms": round(attn_ms, 4),
                    "attention_ms_p10_p50_p90": [round(pct(attn_each, q), 4)
                                                 for q in (0.1, 0.5, 0.9)],
-                   "append_ms": round(codec_ms, 4)},
+                   ("cache_update_ms" if rot else "append_ms"): round(codec_ms, 4)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic},

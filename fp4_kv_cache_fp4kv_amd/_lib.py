@@ -29,7 +29,7 @@ FP4KV_MAX_SLOTS = 64
 EXPORTED = ("fp4kv_strerror", "fp4kv_abi_version", "fp4kv_cache_nbytes", "fp4kv_cache_reset",
             "fp4kv_append_workspace_bytes", "fp4kv_quantize_append", "fp4kv_rope_table",
             "fp4kv_rope_rel", "fp4kv_attention_chunk", "fp4kv_attention_workspace_bytes",
-            "fp4kv_rerotate_window")
+            "fp4kv_rerotate_window", "fp4kv_quantize_append_rotated")
 
 
 class CacheDesc(ctypes.Structure):
@@ -94,6 +94,10 @@ def load() -> ctypes.CDLL:
     lib.fp4kv_rerotate_window.argtypes = [P(CacheDesc), c_i32, c_i32, vp, c_i32, vp,
                                           ctypes.c_size_t, vp]
     lib.fp4kv_rerotate_window.restype = c_int
+    lib.fp4kv_quantize_append_rotated.argtypes = [P(CacheDesc), vp, vp, c_int, c_i32, c_i32,
+                                                  P(c_i32), P(c_i32), vp, c_i32, c_i32, vp,
+                                                  c_i32, vp, ctypes.c_size_t, vp]
+    lib.fp4kv_quantize_append_rotated.restype = c_int
     lib.fp4kv_rope_table.argtypes = [P(c_f), c_i32, c_i32, ctypes.c_double]
     lib.fp4kv_rope_table.restype = c_int
     lib.fp4kv_rope_rel.argtypes = [vp, c_int, vp, c_int, c_i64, c_i32, c_i32, c_i32, c_i32,

@@ -156,6 +156,37 @@ def quantize_append(cache: FP4KVCache, k: torch.Tensor, v: torch.Tensor, frame0:
     check(st, "fp4kv_quantize_append")
 
 
+def quantize_append_rotated(cache: FP4KVCache, k: torch.Tensor, v: torch.Tensor, frame0: int,
+                            n_frames: int, shots: Sequence[int],
+                            tscale: Optional[torch.Tensor] = None,
+                            shot_starts: Optional[Sequence[int]] = None,
+                            f1_prev: Optional[int] = None, f1: Optional[int] = None) -> None:
+    """fp4kv_quantize_append_rotated on the current stream: the whole cache
+    update of an "nvfp4_rot" cache (turn the surviving window keys from the
+    window ending at f1_prev, default frame0, to the one ending at f1,
+    default frame0 + n_frames; append the new keys rotated)."""
+    if cache.kv_format != "nvfp4_rot":
+        raise ValueError("quantize_append_rotated needs a cache with kv_format 'nvfp4_rot'")
+    for t, nm in ((k, "k"), (v, "v")):
+        _require(t, nm, device=cache.device)
+    if k.dtype != v.dtype or k.dtype not in _DTYPES:
+        raise ValueError("k and v must both be float32 or bfloat16")
+    if k.shape != (n_frames * cache.T, cache.H, cache.D) or v.shape != k.shape:
+        raise ValueError(f"k/v must have shape {(n_frames * cache.T, cache.H, cache.D)}")
+    if len(shots) != n_frames:
+        raise ValueError("one shot id per frame")
+    if tscale is not None:
+        _require(tscale, "tscale", torch.float32, cache.device)
+    f1_prev = frame0 if f1_prev is None else f1_prev
+    f1 = frame0 + n_frames if f1 is None else f1
+    st = load().fp4kv_quantize_append_rotated(
+        ctypes.byref(cache.desc), k.data_ptr(), v.data_ptr(), _DTYPES[k.dtype], frame0, n_frames,
+        _i32_array(shots), None if shot_starts is None else _i32_array(shot_starts),
+        _ptr(tscale), int(f1_prev), int(f1), cache.cos_sin.data_ptr(), cache.n_pos,
+        cache.workspace.data_ptr(), cache.workspace.numel(), _stream(cache.device))
+    check(st, "fp4kv_quantize_append_rotated")
+
+
 def rerotate_window(cache: FP4KVCache, f1_from: int, f1_to: int) -> None:
     """fp4kv_rerotate_window on the current stream: turn the surviving window
     keys of an "nvfp4_rot" cache from the window ending at f1_from to the one

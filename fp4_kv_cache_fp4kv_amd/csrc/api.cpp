@@ -67,6 +67,102 @@ int check_buffers(const fp4kv_cache *c) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? FP4KV_OK : FP4KV_EDEVICE; }
 
+// Cache fields of the codec's parameters; no frames, no window move.
+void fill_append(AppendParams &p, const fp4kv_cache *c, void *workspace) {
+  memset(&p, 0, sizeof(p));
+  p.codes[0] = c->k_codes;
+  p.codes[1] = c->v_codes;
+  p.scales[0] = c->k_scales;
+  p.scales[1] = c->v_scales;
+  p.tscale[0] = c->k_tscale;
+  p.tscale[1] = c->v_tscale;
+  p.slot_frame = c->slot_frame;
+  p.slot_shot = c->slot_shot;
+  p.ws_partial = (uint32_t *)workspace;
+  p.ws_rr = (uint32_t *)workspace + kWsRrOffset;
+  p.ws_rr_g = (float *)((uint32_t *)workspace + kWsRrGOffset);
+  p.H = c->n_heads;
+  p.D = c->head_dim;
+  p.T = c->tokens_per_frame;
+  p.stride = c->token_stride;
+  p.Tc = c->tokens_per_frame / c->token_stride;
+  p.Tv = padded_tokens(c);
+  p.S = c->sink_frames;
+  p.W = c->window_frames;
+  p.n_slots = c->sink_frames + c->window_frames;
+  p.half_rot = c->rot_dim / 2;
+  p.bf16_cache = is_bf16(c);
+}
+
+// Validation and parameters shared by the appends (nothing enqueued).
+int prepare_append(AppendParams &p, const fp4kv_cache *c, const void *k, const void *v,
+                   int in_dtype, int32_t frame0, int32_t n_frames, const int32_t *frame_shot,
+                   const int32_t *frame_shot_start, const float *tscale_in, void *workspace,
+                   size_t workspace_bytes) {
+  int st = check_shape(c);
+  if (st) return st;
+  if ((st = check_buffers(c))) return st;
+  if (!k || !v || !frame_shot || !workspace) return FP4KV_EINVAL;
+  if (in_dtype != FP4KV_F32 && in_dtype != FP4KV_BF16) return FP4KV_EINVAL;
+  if (frame0 < 0 || n_frames < 1 || n_frames > FP4KV_MAX_FRAMES) return FP4KV_EINVAL;
+  if (c->sink_per_shot && !frame_shot_start) return FP4KV_EINVAL;
+  int32_t slots[FP4KV_MAX_FRAMES];
+  {  // the frames must land in distinct slots (a chunk, or a bulk re-append)
+    uint64_t used = 0;
+    const int S = c->sink_frames, W = c->window_frames;
+    for (int j = 0; j < n_frames; ++j) {
+      const long long f = (long long)frame0 + j;
+      long long rel = f;   // index from the sink's anchor frame
+      if (c->sink_per_shot) {
+        if (frame_shot_start[j] < 0 || frame_shot_start[j] > f) return FP4KV_EINVAL;
+        rel = f - frame_shot_start[j];
+      }
+      const int slot = rel < S ? (int)rel : S + (int)((f - S) % W);
+      if (used >> slot & 1ull) return FP4KV_EINVAL;
+      used |= 1ull << slot;
+      slots[j] = slot;
+    }
+  }
+  if ((long long)frame0 + n_frames > (1ll << 30)) return FP4KV_EINVAL;
+  if (workspace_bytes < kWsBytes) return FP4KV_ESHAPE;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(workspace)) return FP4KV_EALIGN;
+  if (tscale_in && ((uintptr_t)tscale_in & 3u)) return FP4KV_EALIGN;
+
+  fill_append(p, c, workspace);
+  p.x[0] = k;
+  p.x[1] = v;
+  p.tscale_in = tscale_in;
+  p.frame0 = frame0;
+  p.n_frames = n_frames;
+  p.in_bf16 = in_dtype == FP4KV_BF16;
+  for (int j = 0; j < n_frames; ++j) {
+    p.shot[j] = frame_shot[j];
+    p.slot[j] = slots[j];
+  }
+  return FP4KV_OK;
+}
+
+// Window move f1_from -> f1_to of a cache that stores keys rotated: the
+// window slots to re-encode (rr_slots = 0 when nothing moves or survives).
+int prepare_window_move(AppendParams &p, const fp4kv_cache *c, int32_t f1_from, int32_t f1_to,
+                        const float *cos_sin, int32_t n_pos) {
+  if (c->rot_dim > 0 && !cos_sin) return FP4KV_EINVAL;
+  if ((uintptr_t)cos_sin & 7u) return FP4KV_EALIGN;
+  const int ws0 = window_start(c, f1_from), ws1 = window_start(c, f1_to);
+  const int delta = ws1 - ws0;
+  p.rr_slots = 0;
+  if (delta == 0 || ws1 >= f1_from) return FP4KV_OK;
+  if (c->rot_dim > 0 && delta >= n_pos) return FP4KV_ESHAPE;
+  const long long units = (long long)c->n_heads * (c->tokens_per_frame / c->token_stride) *
+                          (c->head_dim / 16);   // (key row, block) pairs of one slot
+  if (units >= (1ll << 31)) return FP4KV_ESHAPE;
+  p.rr_cs = c->rot_dim > 0 ? cos_sin + (size_t)delta * c->rot_dim : nullptr;
+  p.rr_slots = c->window_frames;
+  p.rr_f_lo = ws1;
+  p.rr_f_hi = f1_from;
+  return FP4KV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -121,66 +217,40 @@ int fp4kv_quantize_append(const fp4kv_cache *c, const void *k, const void *v, in
                           int32_t frame0, int32_t n_frames, const int32_t *frame_shot,
                           const int32_t *frame_shot_start, const float *tscale_in,
                           void *workspace, size_t workspace_bytes, void *stream) {
-  int st = check_shape(c);
-  if (st) return st;
-  if ((st = check_buffers(c))) return st;
-  if (!k || !v || !frame_shot || !workspace) return FP4KV_EINVAL;
-  if (in_dtype != FP4KV_F32 && in_dtype != FP4KV_BF16) return FP4KV_EINVAL;
-  if (frame0 < 0 || n_frames < 1 || n_frames > FP4KV_MAX_FRAMES) return FP4KV_EINVAL;
-  if (c->sink_per_shot && !frame_shot_start) return FP4KV_EINVAL;
-  int32_t slots[FP4KV_MAX_FRAMES];
-  {  // the frames must land in distinct slots (a chunk, or a bulk re-append)
-    uint64_t used = 0;
-    const int S = c->sink_frames, W = c->window_frames;
-    for (int j = 0; j < n_frames; ++j) {
-      const long long f = (long long)frame0 + j;
-      long long rel = f;   // index from the sink's anchor frame
-      if (c->sink_per_shot) {
-        if (frame_shot_start[j] < 0 || frame_shot_start[j] > f) return FP4KV_EINVAL;
-        rel = f - frame_shot_start[j];
-      }
-      const int slot = rel < S ? (int)rel : S + (int)((f - S) % W);
-      if (used >> slot & 1ull) return FP4KV_EINVAL;
-      used |= 1ull << slot;
-      slots[j] = slot;
-    }
-  }
-  if ((long long)frame0 + n_frames > (1ll << 30)) return FP4KV_EINVAL;
-  if (workspace_bytes < kWsBytes) return FP4KV_ESHAPE;
-  if (!aligned16(k) || !aligned16(v) || !aligned16(workspace)) return FP4KV_EALIGN;
-  if (tscale_in && ((uintptr_t)tscale_in & 3u)) return FP4KV_EALIGN;
-
   AppendParams p;
-  memset(&p, 0, sizeof(p));
-  p.x[0] = k;
-  p.x[1] = v;
-  p.codes[0] = c->k_codes;
-  p.codes[1] = c->v_codes;
-  p.scales[0] = c->k_scales;
-  p.scales[1] = c->v_scales;
-  p.tscale[0] = c->k_tscale;
-  p.tscale[1] = c->v_tscale;
-  p.slot_frame = c->slot_frame;
-  p.slot_shot = c->slot_shot;
-  p.tscale_in = tscale_in;
-  p.ws_partial = (uint32_t *)workspace;
-  p.H = c->n_heads;
-  p.D = c->head_dim;
-  p.T = c->tokens_per_frame;
-  p.stride = c->token_stride;
-  p.Tc = c->tokens_per_frame / c->token_stride;
-  p.Tv = padded_tokens(c);
-  p.S = c->sink_frames;
-  p.W = c->window_frames;
-  p.n_slots = c->sink_frames + c->window_frames;
-  p.frame0 = frame0;
-  p.n_frames = n_frames;
-  p.in_bf16 = in_dtype == FP4KV_BF16;
-  p.bf16_cache = is_bf16(c);
-  for (int j = 0; j < n_frames; ++j) {
-    p.shot[j] = frame_shot[j];
-    p.slot[j] = slots[j];
+  int st = prepare_append(p, c, k, v, in_dtype, frame0, n_frames, frame_shot, frame_shot_start,
+                          tscale_in, workspace, workspace_bytes);
+  if (st) return st;
+  return from_hip(launch_append(p, (hipStream_t)stream));
+}
+
+int fp4kv_quantize_append_rotated(const fp4kv_cache *c, const void *k, const void *v,
+                                  int in_dtype, int32_t frame0, int32_t n_frames,
+                                  const int32_t *frame_shot, const int32_t *frame_shot_start,
+                                  const float *tscale_in, int32_t f1_prev, int32_t f1,
+                                  const float *cos_sin, int32_t n_pos, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+  AppendParams p;
+  int st = prepare_append(p, c, k, v, in_dtype, frame0, n_frames, frame_shot, frame_shot_start,
+                          tscale_in, workspace, workspace_bytes);
+  if (st) return st;
+  if (!keys_rotated(c)) return FP4KV_EINVAL;
+  if (f1_prev < 0 || f1 < f1_prev || f1 > (1 << 30) || (long long)frame0 + n_frames > f1)
+    return FP4KV_EINVAL;
+  if ((st = prepare_window_move(p, c, f1_prev, f1, cos_sin, n_pos))) return st;
+  // frames re-encoded by the move and frames written by the append must differ
+  if (p.rr_slots > 0 && frame0 < f1_prev) return FP4KV_EINVAL;
+  const int S = c->sink_frames, ws = window_start(c, f1);
+  for (int j = 0; j < n_frames; ++j) {   // cache-relative position at the window ending at f1
+    const int f = frame0 + j;
+    const int rel = c->sink_per_shot ? f - frame_shot_start[j] : f;
+    const int pos = rel < S ? rel : S + (f - ws);
+    if (pos < 0) return FP4KV_EINVAL;    // neither a sink frame nor in the window
+    if (c->rot_dim > 0 && pos >= n_pos) return FP4KV_ESHAPE;
+    p.pos[j] = pos;
   }
+  p.rotate_keys = 1;
+  p.cos_sin = cos_sin;
   return from_hip(launch_append(p, (hipStream_t)stream));
 }
 
@@ -192,35 +262,13 @@ int fp4kv_rerotate_window(const fp4kv_cache *c, int32_t f1_from, int32_t f1_to,
   if ((st = check_buffers(c))) return st;
   if (!keys_rotated(c)) return FP4KV_EINVAL;
   if (f1_from < 0 || f1_to < f1_from || f1_to > (1 << 30) || !workspace) return FP4KV_EINVAL;
-  if (c->rot_dim > 0 && !cos_sin) return FP4KV_EINVAL;
   if (workspace_bytes < kWsBytes) return FP4KV_ESHAPE;
-  if (!aligned16(workspace) || ((uintptr_t)cos_sin & 7u)) return FP4KV_EALIGN;
-  const int ws0 = window_start(c, f1_from), ws1 = window_start(c, f1_to);
-  const int delta = ws1 - ws0;
-  if (delta == 0 || ws1 >= f1_from) return FP4KV_OK;   // nothing survives a move
-  if (c->rot_dim > 0 && delta >= n_pos) return FP4KV_ESHAPE;
-  const long long units = (long long)c->n_heads * (c->tokens_per_frame / c->token_stride) *
-                          (c->head_dim / 16);   // (key row, block) pairs of one slot
-  if (units >= (1ll << 31)) return FP4KV_ESHAPE;
-
-  RerotParams p;
-  memset(&p, 0, sizeof(p));
-  p.codes = c->k_codes;
-  p.scales = c->k_scales;
-  p.tscale = c->k_tscale;
-  p.slot_frame = c->slot_frame;
-  p.cs = c->rot_dim > 0 ? cos_sin + (size_t)delta * c->rot_dim : nullptr;
-  p.ws_max = (uint32_t *)workspace;
-  p.ws_g = (float *)((uint32_t *)workspace + (size_t)FP4KV_MAX_SLOTS * kRotParts);
-  p.H = c->n_heads;
-  p.D = c->head_dim;
-  p.Tc = c->tokens_per_frame / c->token_stride;
-  p.S = c->sink_frames;
-  p.n_slots = c->sink_frames + c->window_frames;
-  p.half_rot = c->rot_dim / 2;
-  p.f_lo = ws1;
-  p.f_hi = f1_from;
-  return from_hip(launch_rerotate(p, c->window_frames, (hipStream_t)stream));
+  if (!aligned16(workspace)) return FP4KV_EALIGN;
+  AppendParams p;
+  fill_append(p, c, workspace);
+  if ((st = prepare_window_move(p, c, f1_from, f1_to, cos_sin, n_pos))) return st;
+  if (p.rr_slots == 0) return FP4KV_OK;                // nothing survives a move
+  return from_hip(launch_append(p, (hipStream_t)stream));
 }
 
 int fp4kv_rope_table(float *cos_sin, int32_t n_pos, int32_t rot_dim, double base) {

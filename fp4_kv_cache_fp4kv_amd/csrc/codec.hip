@@ -8,8 +8,9 @@
 //   encode_kernel  NVFP4 encode of both tensors straight into their cache
 //                  slots (layouts in include/fp4kv.h), plus the slot metadata.
 // The bf16 baseline format takes one kernel (store_bf16_kernel): a copy into
-// the same ring layout.  Caches that store keys rotated also take the window
-// re-rotation below (rerot_amax_kernel, rerot_encode_kernel).
+// the same ring layout.  For caches that store keys rotated, the same two
+// kernels also turn the appended keys by their positions and re-encode the
+// window slots a window move turns (grid rows / workgroups of their own).
 #include "fp4kv_device.hpp"
 #include "internal.hpp"
 
@@ -59,9 +60,43 @@ __device__ __forceinline__ uint32_t fold_max(uint32_t m, const uint4 &v, bool bf
   return max(m, v.w & 0x7FFFFFFFu);
 }
 
+// Key block b of appended kept token (frame j, tc) and head h, as float32,
+// turned by the frame's position when keys are stored rotated.
+__device__ __forceinline__ void load_key_block(const AppendParams &p, int j, int tc, int h, int b,
+                                              float (&x)[16]);
+
+// Re-encoded window slot s: partial max |decoded key turned back| of this
+// workgroup's share of the slot's (key row, block) pairs.
+__device__ __forceinline__ void rerot_amax(const AppendParams &p, int s, uint32_t *red);
+
 __global__ __launch_bounds__(kThreads) void amax_kernel(AppendParams p) {
   __shared__ uint32_t red[kThreads / 64];
   const int y = blockIdx.y;
+  if (y >= p.amax_tensors) {               // window slots re-encoded by this call
+    rerot_amax(p, p.S + (y - p.amax_tensors), red);
+    return;
+  }
+  if (y == 0 && p.rotate_keys) {           // keys turned before they are stored
+    const int nb = p.D >> 4;
+    const uint32_t units = (uint32_t)(p.n_frames * p.Tc * p.H * nb);
+    uint32_t m = 0;
+    for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < units;
+         u += gridDim.x * kThreads) {
+      const int b = (int)(u % nb);
+      uint32_t rest = u / nb;
+      const int h = (int)(rest % p.H);
+      rest /= p.H;
+      const int tc = (int)(rest % p.Tc);
+      const int j = (int)(rest / p.Tc);
+      float x[16];
+      load_key_block(p, j, tc, h, b, x);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+    }
+    m = block_max_u32(m, red);
+    if (threadIdx.x == 0) p.ws_partial[blockIdx.x] = m;
+    return;
+  }
   const bool bf16 = p.in_bf16;
   const uint32_t row_chunks = (uint32_t)(p.H * p.D * (bf16 ? 2 : 4) / 16);  // one token
   const uint32_t n_chunks = (uint32_t)(p.n_frames * p.Tc) * row_chunks;
@@ -166,6 +201,118 @@ __device__ __forceinline__ void load_block(const AppendParams &p, int y, long lo
 // Slot of appended frame j (computed on the host for either sink mode).
 __device__ __forceinline__ int slot_of(const AppendParams &p, int j) { return p.slot[j]; }
 
+// ---- keys stored rotated (FP4KV_FORMAT_NVFP4_ROT_V1) ----
+// Every turn here feeds the encoder, so it uses rotate_pair_exact (products
+// rounded before the sum).  Pair (2e, 2e+1) of key block b is rotary pair
+// 8b + e; pairs past rot_dim / 2 are kept.
+
+__device__ __forceinline__ void turn_block(float (&x)[16], const float *row, int b, int half_rot,
+                                           bool back) {
+  const float2 *cs = (const float2 *)row;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int pair = 8 * b + e;
+    if (pair < half_rot) {
+      const float2 t = cs[pair];
+      float ra, rb;
+      rotate_pair_exact(x[2 * e], x[2 * e + 1], t.x, back ? -t.y : t.y, ra, rb);
+      x[2 * e] = ra;
+      x[2 * e + 1] = rb;
+    }
+  }
+}
+
+__device__ __forceinline__ void load_key_block(const AppendParams &p, int j, int tc, int h, int b,
+                                              float (&x)[16]) {
+  const long long tok = (long long)j * p.T + (long long)tc * p.stride;
+  load_block(p, 0, (tok * p.H + h) * p.D + b * 16, x);
+  if (p.rotate_keys)
+    turn_block(x, p.cos_sin + (long long)p.pos[j] * (2 * p.half_rot), b, p.half_rot, false);
+}
+
+__device__ __forceinline__ bool rerot_slot(const AppendParams &p, int s) {
+  const int f = p.slot_frame[s];
+  return f >= p.rr_f_lo && f < p.rr_f_hi;
+}
+
+__device__ __forceinline__ long long rerot_row(const AppendParams &p, int s, uint32_t r) {
+  const int h = (int)(r / (uint32_t)p.Tc), tc = (int)(r - (uint32_t)h * (uint32_t)p.Tc);
+  return ((long long)h * p.n_slots + s) * p.Tc + tc;
+}
+
+// Stored key block (codes w, scale code s8, tensor scale g) decoded as
+// sign * fl(fl(E2M1 * E4M3) * g) and turned back by the window move.  The
+// gfx950 FP4 -> float32 conversion with scale 1 gives sign * E2M1 exactly
+// (element 2i from the low nibble of byte i).
+__device__ __forceinline__ void decode_turn(const AppendParams &p, uint2 w, uint32_t s8, float g,
+                                            int b, float (&x)[16]) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const float sv = e4m3_value(s8);
+  const f32x2 e[8] = {   // the byte selector must be a constant
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w.x, 1.0f, 0),
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w.x, 1.0f, 1),
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w.x, 1.0f, 2),
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w.x, 1.0f, 3),
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w.y, 1.0f, 0),
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w.y, 1.0f, 1),
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w.y, 1.0f, 2),
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w.y, 1.0f, 3)};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = (e[i].x * sv) * g;
+    x[2 * i + 1] = (e[i].y * sv) * g;
+  }
+  turn_block(x, p.rr_cs, b, p.half_rot, true);
+}
+
+__device__ __forceinline__ void rerot_amax(const AppendParams &p, int s, uint32_t *red) {
+  if (!rerot_slot(p, s)) return;            // uniform over the workgroup
+  const float g = p.tscale[0][s];
+  const int nb = p.D >> 4;
+  const uint32_t units = (uint32_t)(p.H * p.Tc * nb);
+  uint32_t m = 0;
+  for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < units; u += gridDim.x * kThreads) {
+    const int b = (int)(u % (uint32_t)nb);
+    const long long row = rerot_row(p, s, u / (uint32_t)nb);
+    const uint2 w = *(const uint2 *)(p.codes[0] + row * (p.D >> 1) + b * 8);
+    float x[16];
+    decode_turn(p, w, p.scales[0][row * nb + b], g, b, x);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+  }
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) {
+    p.ws_rr[s * kAmaxBlocks + blockIdx.x] = m;
+    if (blockIdx.x == 0) p.ws_rr_g[s] = g;
+  }
+}
+
+// Workgroup rb of the re-encoding: slot S + rb / rr_blocks, one thread per
+// (key row, block), in place, with g = amax / 2688 of the turned slot.
+__device__ __forceinline__ void rerot_encode(const AppendParams &p, int rb, uint32_t *red) {
+  const int s = p.S + rb / p.rr_blocks, blk = rb % p.rr_blocks;
+  if (!rerot_slot(p, s)) return;            // uniform over the workgroup
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < kAmaxBlocks; i += kThreads) m = max(m, p.ws_rr[s * kAmaxBlocks + i]);
+  m = block_max_u32(m, red);
+  const float amax = __uint_as_float(m);
+  const float g = amax > 0.0f ? __fdiv_rn(amax, 2688.0f) : 1.0f;
+  const float d = 6.0f * g;
+  if (blk == 0 && threadIdx.x == 0) p.tscale[0][s] = g;
+  const int nb = p.D >> 4;
+  const uint32_t units = (uint32_t)(p.H * p.Tc * nb);
+  const uint32_t u = (uint32_t)blk * kThreads + threadIdx.x;
+  if (u >= units) return;
+  const int b = (int)(u % (uint32_t)nb);
+  const long long row = rerot_row(p, s, u / (uint32_t)nb);
+  uint2 *cp = (uint2 *)(p.codes[0] + row * (p.D >> 1) + b * 8);
+  float x[16];
+  decode_turn(p, *cp, p.scales[0][row * nb + b], p.ws_rr_g[s], b, x);
+  uint32_t s8;
+  *cp = encode_block(x, g, d, &s8);
+  p.scales[0][row * nb + b] = (uint8_t)s8;
+}
+
 // One launch encodes both tensors.  Workgroups [0, p.v_blocks) encode the
 // values, dimension-major: one thread per (8 tokens, 16-block) writes one
 // 4-byte word (8 token nibbles) in each of the block's 16 dimension rows plus
@@ -173,9 +320,14 @@ __device__ __forceinline__ int slot_of(const AppendParams &p, int j) { return p.
 // zeros.  They start first because each thread carries 8 blocks.  The other
 // workgroups encode the keys, token-major: one thread per (token, 16-block),
 // blocks fastest, so a wave reads whole rows and writes contiguous bytes.
+// Workgroups past both re-encode the window slots a window move turns.
 __global__ __launch_bounds__(kThreads) void encode_kernel(AppendParams p) {
   const int nb = p.D >> 4;                                   // blocks per row
   __shared__ uint32_t red[kThreads / 64];
+  if ((int)blockIdx.x >= p.v_blocks + p.k_blocks) {
+    rerot_encode(p, (int)blockIdx.x - p.v_blocks - p.k_blocks, red);
+    return;
+  }
   const bool is_v = (int)blockIdx.x < p.v_blocks;
   const int y = is_v ? 1 : 0;
   const float g = p.tscale_in ? p.tscale_in[y] : tensor_scale(p, y, red);
@@ -202,9 +354,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(AppendParams p) {
     const int j = (int)(rest % p.n_frames);
     const int h = (int)(rest / p.n_frames);
     const int slot = slot_of(p, j);
-    const long long tok = (long long)j * p.T + (long long)tc * p.stride;
     float x[16];
-    load_block(p, 0, (tok * p.H + h) * p.D + b * 16, x);
+    load_key_block(p, j, tc, h, b, x);
     uint32_t s8;
     const uint2 packed = encode_block(x, g, d, &s8);
     const long long row = ((long long)h * p.n_slots + slot) * p.Tc + tc;
@@ -336,102 +487,6 @@ __global__ __launch_bounds__(kThreads) void store_bf16_kernel(AppendParams p) {
   }
 }
 
-// ---- window re-rotation (keys stored rotated, FP4KV_FORMAT_NVFP4_ROT_V1) ----
-//
-// When the window start moves by delta, every surviving window key is turned
-// by -delta in place: decode, rotate in float32, re-encode with a fresh
-// tensor scale over the slot (all heads).  Two kernels, grid.y = window slot:
-//   rerot_amax_kernel    grid (kRotParts, W): partial max |turned key| per
-//                        workgroup of a slot, plus the slot's old scale;
-//   rerot_encode_kernel  one thread per (key row, 16-block): decode, turn,
-//                        encode in place with g = amax / 2688.
-// A workgroup whose slot holds no frame to turn returns at once.
-
-__device__ __forceinline__ bool rerot_slot(const RerotParams &p, int s) {
-  const int f = p.slot_frame[s];
-  return f >= p.f_lo && f < p.f_hi;
-}
-
-// Key block b of a row: decode x = sign * fl(fl(E2M1 * E4M3) * g), then turn
-// pair (2e, 2e+1), rotary pair 8b + e, by -delta with the exact float32
-// arithmetic; pairs past rot_dim / 2 are kept.
-__device__ __forceinline__ void decode_turn(const RerotParams &p, uint2 w, uint32_t s8, float g,
-                                            int b, float (&x)[16]) {
-  const float sv = e4m3_value(s8);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t nib = ((i < 8 ? w.x : w.y) >> (4 * (i & 7))) & 0xFu;
-    const float v = (e2m1_value(nib & 7u) * sv) * g;
-    x[i] = (nib & 8u) ? -v : v;
-  }
-  const float2 *cs = (const float2 *)p.cs;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int pair = 8 * b + e;
-    if (pair < p.half_rot) {
-      const float2 t = cs[pair];
-      float ra, rb;
-      rotate_pair_exact(x[2 * e], x[2 * e + 1], t.x, -t.y, ra, rb);
-      x[2 * e] = ra;
-      x[2 * e + 1] = rb;
-    }
-  }
-}
-
-__device__ __forceinline__ long long rerot_row(const RerotParams &p, int s, uint32_t r) {
-  const int h = (int)(r / (uint32_t)p.Tc), tc = (int)(r - (uint32_t)h * (uint32_t)p.Tc);
-  return ((long long)h * p.n_slots + s) * p.Tc + tc;
-}
-
-__global__ __launch_bounds__(kThreads) void rerot_amax_kernel(RerotParams p) {
-  __shared__ uint32_t red[kThreads / 64];
-  const int s = p.S + (int)blockIdx.y;
-  if (!rerot_slot(p, s)) return;
-  const float g = p.tscale[s];
-  const int nb = p.D >> 4;
-  const uint32_t units = (uint32_t)(p.H * p.Tc * nb);
-  uint32_t m = 0;
-  for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < units; u += gridDim.x * kThreads) {
-    const int b = (int)(u % (uint32_t)nb);
-    const long long row = rerot_row(p, s, u / (uint32_t)nb);
-    const uint2 w = *(const uint2 *)(p.codes + row * (p.D >> 1) + b * 8);
-    float x[16];
-    decode_turn(p, w, p.scales[row * nb + b], g, b, x);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
-  }
-  m = block_max_u32(m, red);
-  if (threadIdx.x == 0) {
-    p.ws_max[s * kRotParts + blockIdx.x] = m;
-    if (blockIdx.x == 0) p.ws_g[s] = g;
-  }
-}
-
-__global__ __launch_bounds__(kThreads) void rerot_encode_kernel(RerotParams p) {
-  __shared__ uint32_t red[kThreads / 64];
-  const int s = p.S + (int)blockIdx.y;
-  if (!rerot_slot(p, s)) return;
-  uint32_t m = 0;
-  for (int i = threadIdx.x; i < kRotParts; i += kThreads) m = max(m, p.ws_max[s * kRotParts + i]);
-  m = block_max_u32(m, red);
-  const float amax = __uint_as_float(m);
-  const float g = amax > 0.0f ? __fdiv_rn(amax, 2688.0f) : 1.0f;
-  const float d = 6.0f * g;
-  if (blockIdx.x == 0 && threadIdx.x == 0) p.tscale[s] = g;
-  const int nb = p.D >> 4;
-  const uint32_t units = (uint32_t)(p.H * p.Tc * nb);
-  const uint32_t u = blockIdx.x * kThreads + threadIdx.x;
-  if (u >= units) return;
-  const int b = (int)(u % (uint32_t)nb);
-  const long long row = rerot_row(p, s, u / (uint32_t)nb);
-  uint2 *cp = (uint2 *)(p.codes + row * (p.D >> 1) + b * 8);
-  float x[16];
-  decode_turn(p, *cp, p.scales[row * nb + b], p.ws_g[s], b, x);
-  uint32_t s8;
-  *cp = encode_block(x, g, d, &s8);
-  p.scales[row * nb + b] = (uint8_t)s8;
-}
-
 __global__ void reset_kernel(int32_t *slot_frame, int32_t *slot_shot, float *kt, float *vt, int n) {
   const int i = threadIdx.x;
   if (i < n) {
@@ -464,25 +519,20 @@ hipError_t launch_append(const AppendParams &p_in, hipStream_t s) {
   }
   const long long k_units = (long long)p.H * p.n_frames * p.Tc * (p.D >> 4);
   const long long v_units = (long long)p.H * p.n_frames * (p.Tv >> 3) * (p.D >> 4);
+  const long long rr_units = (long long)p.H * p.Tc * (p.D >> 4);   // per re-encoded slot
   p.v_blocks = (int)((v_units + kThreads - 1) / kThreads);
-  const long long k_blocks = (k_units + kThreads - 1) / kThreads;
-  if (!p.tscale_in) {
-    hipLaunchKernelGGL(amax_kernel, dim3(kAmaxBlocks, 2), dim3(kThreads), 0, s, p);
+  p.k_blocks = (int)((k_units + kThreads - 1) / kThreads);
+  p.rr_blocks = p.rr_slots > 0 ? (int)((rr_units + kThreads - 1) / kThreads) : 0;
+  p.amax_tensors = (p.n_frames > 0 && !p.tscale_in) ? 2 : 0;
+  const int amax_y = p.amax_tensors + p.rr_slots;
+  if (amax_y > 0) {
+    hipLaunchKernelGGL(amax_kernel, dim3(kAmaxBlocks, amax_y), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(encode_kernel, dim3((unsigned)(p.v_blocks + k_blocks)), dim3(kThreads), 0, s,
-                     p);
-  return hipGetLastError();
-}
-
-hipError_t launch_rerotate(const RerotParams &p, int window_slots, hipStream_t s) {
-  const long long units = (long long)p.H * p.Tc * (p.D >> 4);
-  hipLaunchKernelGGL(rerot_amax_kernel, dim3(kRotParts, window_slots), dim3(kThreads), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const unsigned blocks = (unsigned)((units + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL(rerot_encode_kernel, dim3(blocks, window_slots), dim3(kThreads), 0, s, p);
+  const long long blocks = (long long)p.v_blocks + p.k_blocks + (long long)p.rr_slots * p.rr_blocks;
+  if (blocks > 0)
+    hipLaunchKernelGGL(encode_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -11,16 +11,14 @@ namespace fp4kv {
 // Number of partial maxima per tensor in the append workspace.
 constexpr int kAmaxBlocks = 256;
 
-// Partial maxima per cache slot in the re-rotation's amax pass.
-constexpr int kRotParts = 32;
-
-// Workspace of fp4kv_quantize_append: uint32 partial maxima [2][kAmaxBlocks]
-// (float32 bit patterns of max |x| per workgroup of the amax pass).  The
-// window re-rotation uses the same workspace: partial maxima
-// [FP4KV_MAX_SLOTS][kRotParts], then the old tensor scales [FP4KV_MAX_SLOTS].
-constexpr size_t kAppendWsBytes = 2 * kAmaxBlocks * sizeof(uint32_t);
-constexpr size_t kRotWsBytes = (size_t)FP4KV_MAX_SLOTS * (kRotParts + 1) * sizeof(uint32_t);
-constexpr size_t kWsBytes = kAppendWsBytes > kRotWsBytes ? kAppendWsBytes : kRotWsBytes;
+// Workspace of the append and the window re-rotation: uint32 partial maxima
+// (float32 bit patterns of max |x| per workgroup of the amax pass) of the
+// appended K and V [2][kAmaxBlocks], then of each re-encoded window slot
+// [FP4KV_MAX_SLOTS][kAmaxBlocks], then the slots' previous key tensor scales
+// [FP4KV_MAX_SLOTS] (float32).
+constexpr size_t kWsRrOffset = 2 * kAmaxBlocks;                        // in uint32
+constexpr size_t kWsRrGOffset = kWsRrOffset + (size_t)FP4KV_MAX_SLOTS * kAmaxBlocks;
+constexpr size_t kWsBytes = (kWsRrGOffset + FP4KV_MAX_SLOTS) * sizeof(uint32_t);
 
 struct AppendParams {
   const void *x[2];        // K, V inputs [n_frames*T][H][D]
@@ -34,20 +32,21 @@ struct AppendParams {
   int in_bf16;
   int bf16_cache;          // FP4KV_FORMAT_BF16_V1: store bf16, no quantization
   int v_blocks;            // workgroups of the value pass in encode_kernel
+  int k_blocks;            // workgroups of the key pass
+  int amax_tensors;        // 2 when the amax pass covers the appended K and V, else 0
+  // Keys stored rotated (FP4KV_FORMAT_NVFP4_ROT_V1).  half_rot > 0 with
+  // rotate_keys: appended keys are turned by their frame's position first.
+  // rr_slots > 0: the window slots whose frame f has rr_f_lo <= f < rr_f_hi
+  // are decoded, turned back by table row rr_cs and encoded again in place.
+  const float *cos_sin;    // rotary table [n_pos][half_rot][2]
+  const float *rr_cs;      // table row of the window move (cos, sin) [half_rot]
+  uint32_t *ws_rr;         // [FP4KV_MAX_SLOTS][kAmaxBlocks] partial maxima
+  float *ws_rr_g;          // [FP4KV_MAX_SLOTS] key tensor scales before the call
+  int half_rot, rotate_keys;
+  int rr_slots, rr_f_lo, rr_f_hi, rr_blocks;
   int32_t shot[FP4KV_MAX_FRAMES];
   int32_t slot[FP4KV_MAX_FRAMES];   // cache slot of each frame (host-computed)
-};
-
-// Window re-rotation of keys stored rotated (FP4KV_FORMAT_NVFP4_ROT_V1).
-struct RerotParams {
-  uint8_t *codes, *scales;   // key codes and block scales
-  float *tscale;             // key tensor scales [n_slots]
-  const int32_t *slot_frame;
-  const float *cs;           // table row delta: (cos, sin) per rotary pair
-  uint32_t *ws_max;          // [n_slots][kRotParts] partial maxima
-  float *ws_g;               // [n_slots] tensor scales before the call
-  int H, D, Tc, S, n_slots, half_rot;
-  int f_lo, f_hi;            // window frames f_lo <= f < f_hi are turned
+  int32_t pos[FP4KV_MAX_FRAMES];    // position of each frame (rotated keys)
 };
 
 struct RopeParams {
@@ -79,7 +78,6 @@ struct AttnParams {
 
 hipError_t launch_cache_reset(const fp4kv_cache &c, hipStream_t s);
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
-hipError_t launch_rerotate(const RerotParams &p, int window_slots, hipStream_t s);
 hipError_t launch_rope(const RopeParams &p, hipStream_t s);
 hipError_t launch_attention(const AttnParams &p, int head_dim, int out_f32, hipStream_t s);
 

@@ -96,12 +96,13 @@ extern "C" {
  * KV-cache relative RoPE; refft.com, question "How do KV-cache relative
  * RoPE and TriAttention work together ..."): the same buffers and layout,
  * but k_codes hold keys ALREADY rotated by their cache-relative position
- * (pos(f) below, for the window that ends after the append).  The caller
- * rotates new keys with fp4kv_rope_rel (float32 output) before
- * fp4kv_quantize_append, and calls fp4kv_rerotate_window before each append
- * that moves the window start, which turns the surviving window keys in
- * place.  Attention then uses keys as stored.  Each window key is
- * re-encoded once per step it survives, which adds rounding error.
+ * (pos(f) below, for the window that ends after the append).  One call per
+ * step, fp4kv_quantize_append_rotated, turns the surviving window keys and
+ * appends the new keys rotated; the same result comes from
+ * fp4kv_rerotate_window, fp4kv_rope_rel of the new keys (float32 output)
+ * and fp4kv_quantize_append.  Attention then uses keys as stored.  Each
+ * window key is re-encoded once per step it survives, which adds rounding
+ * error.
  *
  * NVFP4 blocks are 16 consecutive elements along D for keys and values.
  * Keys are stored token-major; values are stored dimension-major so that the
@@ -216,6 +217,33 @@ int fp4kv_quantize_append(const fp4kv_cache *c, const void *k, const void *v,
                           const int32_t *frame_shot, const int32_t *frame_shot_start,
                           const float *tscale_in, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/*
+ * fp4kv_quantize_append_rotated - the cache update of a
+ * FP4KV_FORMAT_NVFP4_ROT_V1 cache in one call (two kernels): the window
+ * move of fp4kv_rerotate_window(c, f1_prev, f1), then the append of
+ * fp4kv_quantize_append with each key turned first by its frame's position
+ * at the window ending at f1 (pair (2i, 2i+1), i < rot_dim/2:
+ * (a, b) -> (fl(fl(a c) - fl(b s)), fl(fl(a s) + fl(b c))), float32, from
+ * the float32 value of the input); the key tensor scale is taken over the
+ * turned keys.  Arguments as in fp4kv_quantize_append, plus:
+ *   f1_prev    window end the stored rotations belong to (normally frame0);
+ *   f1         window end after the call (normally frame0 + n_frames);
+ *              0 <= f1_prev <= f1, frame0 + n_frames <= f1.  Every frame
+ *              must be a sink frame or lie in the window [ws(f1), f1).
+ *   cos_sin    device table (fp4kv_rope_table, cache->rot_dim) with n_pos
+ *              rows, more than any position and the window move; may be
+ *              NULL when rot_dim = 0.
+ * When the window start moves, the appended frames must all be >= f1_prev
+ * (the re-encoded frames and the written frames are then distinct).
+ * Errors: FP4KV_EINVAL for a cache of another format.
+ */
+int fp4kv_quantize_append_rotated(const fp4kv_cache *c, const void *k, const void *v,
+                                  int in_dtype, int32_t frame0, int32_t n_frames,
+                                  const int32_t *frame_shot, const int32_t *frame_shot_start,
+                                  const float *tscale_in, int32_t f1_prev, int32_t f1,
+                                  const float *cos_sin, int32_t n_pos, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /*
  * fp4kv_rerotate_window - move the stored key rotations of a

@@ -154,6 +154,30 @@ def test_rerotate_validation_before_launch():
     assert call(c=r0, f0=6, f1=9, cs=None) == 0       # rot_dim 0 needs no table
 
 
+def test_append_rotated_validation_before_launch():
+    lib = _lib.load()
+    c = _desc(format_tag=_lib.FP4KV_FORMAT_NVFP4_ROT_V1)     # S = 3, W = 12, C = 3
+    A, Wk = 0x100000, 0x4000000
+    shots = (ctypes.c_int32 * 4)(0, 0, 0, 0)
+    ws = lib.fp4kv_append_workspace_bytes()
+    call = lambda **kw: lib.fp4kv_quantize_append_rotated(
+        ctypes.byref(kw.get("c", c)), A, A, 1, kw.get("f0", 15), kw.get("n", 3), shots, None,
+        None, kw.get("fp", 15), kw.get("f1", 18), kw.get("cs", A), kw.get("npos", 15),
+        kw.get("ws", Wk), ws, None)
+    assert call(c=_desc()) == -1                     # keys stored before rotation
+    assert call(fp=-1) == -1
+    assert call(fp=19) == -1                         # f1_prev > f1
+    assert call(f1=17) == -1                         # frames past the window end
+    assert call(fp=16) == -1                         # re-encoded and written frames overlap
+    assert call(cs=None) == -1
+    assert call(cs=A + 4) == -3
+    assert call(npos=3) == -2                        # window move of 3 needs row 3
+    assert call(npos=12) == -2                       # position 14 of frame 17
+    assert call(f0=1, n=3, fp=21, f1=21) == -1       # frame 3 is not in the window [9, 21)
+    assert call(f0=3, n=3, fp=21, f1=21) == -1       # frames 3..5 left the window
+    assert call(n=0) == -1
+
+
 def test_stride_must_divide_tokens():
     lib = _lib.load()
     out = (ctypes.c_size_t * 6)()

@@ -2,11 +2,12 @@
 keys stored rotated; fp4kv_rerotate_window turns the surviving window keys
 when the window start moves) against the oracle's OracleCacheRot.
 
-Each step runs, on the GPU: rerotate_window(f0 -> f0 + n), rope_rel of the
-new keys and queries at their positions, quantize_append of the rotated
-keys, attention.  The rotations and re-encodings decide codes, so the cache
-bytes are compared bit-exact after every checked step; attention within
-max-abs 1e-2 / mean-abs 1e-3 (float32 output)."""
+Each step runs, on the GPU, either the composed calls (rerotate_window
+f0 -> f0 + n, rope_rel of the new keys at their positions, quantize_append
+of the rotated keys) or the one-call quantize_append_rotated, then rope_rel
+of the queries and attention.  The rotations and re-encodings decide codes,
+so the cache bytes are compared bit-exact after every checked step;
+attention within max-abs 1e-2 / mean-abs 1e-3 (float32 output)."""
 import dataclasses
 
 import numpy as np
@@ -29,7 +30,7 @@ def _shot_start(w, f):
     return f
 
 
-def _run(w, steps, rot_dim=None, per_shot=False, rows=None, heads=None):
+def _run(w, steps, rot_dim=None, per_shot=False, rows=None, heads=None, fused=False):
     from fp4_kv_cache_fp4kv_amd import api
     gc = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride, rot_dim,
                         kv_format="nvfp4_rot", sink_per_shot=per_shot)
@@ -42,22 +43,28 @@ def _run(w, steps, rot_dim=None, per_shot=False, rows=None, heads=None):
     for c in range(max(steps) + 1):
         f0, n = w.chunk_frames(c)
         f1 = f0 + n
-        (q, qb), (k, kb), (v, _) = step_inputs(w, c)
+        (q, qb), (k, kb), (v, vb) = step_inputs(w, c)
         shots = shots_of(w, f0, n)
         fss = [_shot_start(w, f) for f in range(f0, f1)] if per_shot else None
         moved += len(oc.rerotate(f0, f1))
         oc.append_rotated(k, v, f0, n, shots, shot_starts=fss)
-        say(f"rotated {w.name} step {c} frames {f0}..{f1 - 1} rot_dim {gc.rot_dim}")
-        api.rerotate_window(gc, f0, f1)
+        say(f"rotated {w.name} step {c} frames {f0}..{f1 - 1} rot_dim {gc.rot_dim} "
+            f"{'one call' if fused else 'composed'}")
         kd, qd = device_tensor(k, kb), device_tensor(q, qb)
+        if fused:
+            api.quantize_append_rotated(gc, kd, device_tensor(v, vb), f0, n, shots,
+                                        shot_starts=fss)
+        else:
+            api.rerotate_window(gc, f0, f1)
         for j in range(n):   # per frame: positions jump at a cut with per-shot sinks
             pos = api.frame_position(w.S, w.W, f0 + j, f1, fss[j] if per_shot else None)
             r = slice(j * w.T, (j + 1) * w.T)
-            api.rope_rel(kd[r], pos, w.T, gc.cos_sin, rot_dim=gc.rot_dim, out=krot[r])
+            if not fused:
+                api.rope_rel(kd[r], pos, w.T, gc.cos_sin, rot_dim=gc.rot_dim, out=krot[r])
             api.rope_rel(qd[r], pos, w.T, gc.cos_sin, rot_dim=gc.rot_dim, out=qrot[r])
-        # values go in as float32 (bf16 inputs are exact in float32)
-        api.quantize_append(gc, krot[:n * w.T], device_tensor(v, None), f0, n, shots,
-                            shot_starts=fss)
+        if not fused:   # values go in as float32 (bf16 inputs are exact in float32)
+            api.quantize_append(gc, krot[:n * w.T], device_tensor(v, None), f0, n, shots,
+                                shot_starts=fss)
         o = api.attention_chunk(gc, qrot[:n * w.T], f0, n, shots, out_dtype=torch.float32)
         torch.cuda.synchronize()
         if c not in steps:
@@ -73,27 +80,57 @@ def _run(w, steps, rot_dim=None, per_shot=False, rows=None, heads=None):
     assert moved > 0, "the stream never moved the window"
 
 
-def test_rotated_d64_stride2_bf16_wrapping():
+FUSED = pytest.mark.parametrize("fused", [False, True], ids=["composed", "one_call"])
+
+
+@FUSED
+def test_rotated_d64_stride2_bf16_wrapping(fused):
     w = wl.Workload("rot64", H=3, D=64, T=40, C=2, S=1, W=5, n_frames=21, seed=51,
                     token_stride=2)
-    _run(w, list(range(w.n_chunks)))
+    _run(w, list(range(w.n_chunks)), fused=fused)
 
 
-def test_rotated_d128_partial_rot_dim_outliers():
+@FUSED
+def test_rotated_d128_partial_rot_dim_outliers(fused):
     w = wl.Workload("rot128", H=2, D=128, T=100, C=3, S=2, W=7, n_frames=28, seed=52,
                     dtype="f32", outlier_p=0.01, outlier_scale=20.0)
-    _run(w, [3, 4, 5, 8, 9], rot_dim=96)
+    _run(w, [3, 4, 5, 8, 9], rot_dim=96, fused=fused)
 
 
-def test_rotated_rot_dim_zero():
+@FUSED
+def test_rotated_rot_dim_zero(fused):
     w = wl.Workload("rot0", H=2, D=64, T=24, C=3, S=2, W=6, n_frames=20, seed=53, dtype="f32")
-    _run(w, [3, 4, 6], rot_dim=0)
+    _run(w, [3, 4, 6], rot_dim=0, fused=fused)
 
 
-def test_rotated_per_shot_sinks_cuts_inside_chunks():
+@FUSED
+def test_rotated_per_shot_sinks_cuts_inside_chunks(fused):
     w = wl.Workload("rotshot", H=2, D=64, T=32, C=3, S=2, W=6, n_frames=30, seed=54,
                     shot_len=7)
-    _run(w, list(range(w.n_chunks)), per_shot=True)
+    _run(w, list(range(w.n_chunks)), per_shot=True, fused=fused)
+
+
+def test_rotated_one_call_caller_scales_and_partial_chunk():
+    # caller-supplied tensor scales (no amax pass for the append, but one for
+    # the window move) and a short last chunk
+    from fp4_kv_cache_fp4kv_amd import api
+    w = wl.Workload("rotts", H=2, D=64, T=16, C=3, S=1, W=6, n_frames=17, seed=55, dtype="f32")
+    gc = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, kv_format="nvfp4_rot")
+    oc = OracleCacheRot(w.H, w.D, w.T, w.C, w.S, w.W)
+    ts = np.array([0.0021, 0.0017], np.float32)
+    tsd = torch.from_numpy(ts).to("cuda:0")
+    for c in range(w.n_chunks):
+        f0, n = w.chunk_frames(c)
+        (_, _), (k, _), (v, _) = step_inputs(w, c)
+        shots = shots_of(w, f0, n)
+        oc.rerotate(f0, f0 + n)
+        oc.append_rotated(k, v, f0, n, shots, tscale=ts)
+        say(f"rotated caller scales step {c} frames {f0}..{f0 + n - 1}")
+        api.quantize_append_rotated(gc, device_tensor(k, None), device_tensor(v, None), f0, n,
+                                    shots, tscale=tsd)
+        torch.cuda.synchronize()
+        bad = compare_cache(gc, oc)
+        assert not bad, (c, bad)
 
 
 def test_rotated_full_size_l13b_sampled():
@@ -103,4 +140,4 @@ def test_rotated_full_size_l13b_sampled():
     nq = w.C * w.T
     rows = np.unique(np.concatenate([[0, w.T - 1, w.T, 2 * w.T, nq - 1],
                                      rng.integers(0, nq, 40)]))
-    _run(w, [5, 6], rows=rows, heads=[0, w.H - 1])
+    _run(w, [5, 6], rows=rows, heads=[0, w.H - 1], fused=True)
