@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters")
+    ap.add_argument("--codec-sweep", action="store_true",
+                    help="only time the append at 3, 6 and 15 frames of the workload next to "
+                         "plain device copies of similar sizes, print one JSON line, and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (5 times), to calibrate the "
                          "FETCH_SIZE / WRITE_SIZE counters, and exit")
@@ -77,6 +80,47 @@ def copy_calibration(nbytes):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": src.numel() * 4, "launches": 5}), flush=True)
+
+
+def codec_sweep(w):
+    """Append bandwidth against size, next to what a plain device copy reaches
+    at similar sizes (both timed with HIP events over 30 calls, inputs
+    resident): the ceiling a two-pass append can approach at a given size."""
+    import torch
+
+    from fp4_kv_cache_fp4kv_amd import api
+
+    def tm(fn, reps=30):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3     # microseconds
+
+    out = {"workload": workload_desc(w), "copy": {}, "append": {}}
+    for mb in (37, 74, 184, 512):                   # read mb, write mb
+        src = torch.empty(mb * 500_000, dtype=torch.bfloat16, device="cuda:0").normal_()
+        dst = torch.empty_like(src)
+        us = tm(lambda: dst.copy_(src))
+        out["copy"][f"{mb}MB"] = {"us": round(us, 2), "GB/s": round(2 * mb * 1e6 / us / 1e3, 1)}
+        del src, dst
+    gc = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride)
+    es = 2 if w.dtype == "bf16" else 4
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    for nf in sorted({w.C, 2 * w.C, w.S + w.W}):
+        k = torch.randn(nf * w.T, w.H, w.D, device="cuda:0").to(dt)
+        v = torch.randn(nf * w.T, w.H, w.D, device="cuda:0").to(dt)
+        us = tm(lambda: api.quantize_append(gc, k, v, 0, nf, [0] * nf))
+        kept = 2 * nf * w.Tc * w.H * w.D
+        b = kept * es + kept * (0.5 + 1.0 / 16.0)
+        out["append"][f"{nf}_frames"] = {"us": round(us, 2), "MB": round(b / 1e6, 1),
+                                         "GB/s": round(b / us / 1e3, 1)}
+    print(json.dumps(out), flush=True)
 
 
 def workload_desc(w):
@@ -164,6 +208,10 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.codec_sweep:
+        from fp4_kv_cache_fp4kv_amd import workloads as wl
+        codec_sweep(wl.WORKLOADS[args.workload])
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
