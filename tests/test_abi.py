@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp4kv.h")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
-                                reason="libfp4kv.so not built (run __graft_entry__.build())")
+                                reason="libfp4kv.so not built (python -m fp4_kv_cache_fp4kv_amd.build)")
 
 
 def declared_functions():
