@@ -53,8 +53,9 @@ def parse():
     ap.add_argument("--sink-per-shot", action="store_true",
                     help="per-shot attention sinks (each shot re-anchors the sink)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                    help="per-launch HBM bytes measured with rocprofv3 counters")
+    ap.add_argument("--traffic-json", default=None,
+                    help="per-launch HBM bytes measured with rocprofv3 counters "
+                         "(default: profiles/traffic_<workload>.json)")
     ap.add_argument("--codec-sweep", action="store_true",
                     help="only time the append at 3, 6 and 15 frames of the workload next to "
                          "plain device copies of similar sizes, print one JSON line, and exit")
@@ -332,9 +333,10 @@ def main():
     # the kernel source they were taken on
     traffic = None
     try:
-        tj = json.load(open(args.traffic_json))
+        tj = json.load(open(args.traffic_json or
+                            os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")))
         if (tj.get("workload") == w.name and tj.get("source_hash") == attention_source_hash()
-                and args.kv == "nvfp4"):
+                and args.kv == "nvfp4" and not args.sink_per_shot):
             traffic = tj.get("attention_bytes_per_launch")
     except (OSError, ValueError):
         pass
