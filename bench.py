@@ -52,6 +52,9 @@ def parse():
                          "moves), or the bf16 baseline")
     ap.add_argument("--sink-per-shot", action="store_true",
                     help="per-shot attention sinks (each shot re-anchors the sink)")
+    ap.add_argument("--workgroups", type=int, default=0,
+                    help="attention workgroups (0: the library's default, one per compute unit "
+                         "with at least 4 key tiles each)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=None,
                     help="per-launch HBM bytes measured with rocprofv3 counters "
@@ -283,7 +286,7 @@ def main():
         rope(q, qrot)
         if record:
             e[2].record()
-        api.attention_chunk(gc, qrot, f0, w.C, shots, out=out)
+        api.attention_chunk(gc, qrot, f0, w.C, shots, out=out, n_workgroups=args.workgroups)
         if record:
             e[3].record()
             ev["c0"].append(e[0]); ev["c1"].append(e[1])
@@ -356,6 +359,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_desc(w), "kv_format": args.kv,
                    "sink": "per_shot" if args.sink_per_shot else "stream", "query_rows": Nq,
+                   "workgroups": args.workgroups or "default",
                    "keys": Nk,
                    "frames_per_step": w.C, "attention_ms": round(attn_ms, 4),
                    "attention_only_frames_per_s": round(w.C / (attn_ms * 1e-3), 1),
