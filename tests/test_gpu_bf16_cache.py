@@ -82,3 +82,42 @@ def test_bf16_cache_full_size_sampled():
     rows = np.unique(np.concatenate([[0, 255, 256, w.T - 1, w.T, nq - 1],
                                      rng.integers(0, nq, 40)]))
     _run(w, [(w.S + w.W) // w.C - 1], rows=rows, heads=[0, w.H - 1])
+
+
+def test_bf16_cache_per_shot_sinks_cuts_inside_chunks():
+    # the baseline format with per-shot sinks: slots chosen per frame on the
+    # host, sink visibility per shot in the kernel's frame list
+    from fp4_kv_cache_fp4kv_amd import api
+    w = wl.Workload("bf_shots", H=2, D=64, T=24, C=3, S=2, W=6, n_frames=26, seed=71,
+                    shot_len=7)
+    gc = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride, kv_format="bf16",
+                        sink_per_shot=True)
+    oc = OracleCacheBF16.for_workload(w, sink_per_shot=True)
+
+    def shot_start(f):
+        s = w.shot_of(f)
+        while f > 0 and w.shot_of(f - 1) == s:
+            f -= 1
+        return f
+    qrot = torch.empty((w.C * w.T, w.H, w.D), dtype=torch.float32, device="cuda:0")
+    for c in range(w.n_chunks):
+        f0, n = w.chunk_frames(c)
+        (q, qb), (k, kb), (v, vb) = step_inputs(w, c)
+        shots = shots_of(w, f0, n)
+        fss = [shot_start(f) for f in range(f0, f0 + n)]
+        oc.append(k, v, f0, n, shots, shot_starts=fss)
+        say(f"bf16 cache per-shot step {c} shot starts {fss}")
+        api.quantize_append(gc, device_tensor(k, kb), device_tensor(v, vb), f0, n, shots,
+                            shot_starts=fss)
+        qd = device_tensor(q, qb)
+        for j in range(n):
+            rows = slice(j * w.T, (j + 1) * w.T)
+            api.rope_rel(qd[rows], api.frame_position(w.S, w.W, f0 + j, f0 + n, fss[j]), w.T,
+                         gc.cos_sin, out=qrot[rows])
+        o = api.attention_chunk(gc, qrot[:n * w.T], f0, n, shots, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert not _compare(gc, oc), (c, _compare(gc, oc))
+        ref = oc.attention(q, f0, n, shots, q_shot_starts=fss)
+        mx, mn = err_stats(o.cpu().numpy(), ref)
+        say(f"  max-abs {mx:.3e} mean-abs {mn:.3e}")
+        assert mx <= MAX_ABS and mn <= MEAN_ABS, (c, mx, mn)
