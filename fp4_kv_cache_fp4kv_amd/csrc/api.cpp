@@ -39,6 +39,10 @@ int check_shape(const fp4kv_cache *c) {
   if (c->sink_frames + c->window_frames > FP4KV_MAX_SLOTS) return FP4KV_ESHAPE;
   if (c->rot_dim < 0 || c->rot_dim > c->head_dim || (c->rot_dim & 1)) return FP4KV_EINVAL;
   if (c->sink_per_shot != 0 && c->sink_per_shot != 1) return FP4KV_EINVAL;
+  // One (head, slot) of the largest layout (bf16 values, D x Tv) stays below
+  // 2 GiB: the kernels address inside a slot with 32-bit offsets and sizes.
+  const long long tv = ((long long)(c->tokens_per_frame / c->token_stride) + 31) / 32 * 32;
+  if (2ll * c->head_dim * tv >= (1ll << 31)) return FP4KV_ESHAPE;
   const long long rows = (long long)c->n_heads * (c->sink_frames + c->window_frames) *
                          (c->tokens_per_frame / c->token_stride);
   if (rows * c->head_dim > (1ll << 40)) return FP4KV_ESHAPE;

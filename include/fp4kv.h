@@ -127,6 +127,11 @@ extern "C" {
  * A decoded element is sign * E2M1(code) * E4M3(scale) * tensor_scale.
  * These buffers are opaque bytes: never cast or convert them.
  *
+ * Size limits (FP4KV_ESHAPE otherwise): one (head, slot) of the bf16 value
+ * layout, 2 * D * Tv bytes, stays below 2^31 (Tv <= 8388576 at D = 128,
+ * 16777184 at D = 64), and the whole cache holds at most 2^40 elements per
+ * code array (H * (S + W) * Tc * D).
+ *
  * Baseline format FP4KV_FORMAT_BF16_V1 (the unquantized cache that NVFP4 is
  * measured against; same ring, slots and attention): k_codes holds bf16
  * [H][S+W][Tc][D], v_codes bf16 [H][S+W][D][Tv] (padding tokens zero),

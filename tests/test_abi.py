@@ -94,6 +94,9 @@ def test_cache_nbytes():
     ("n_heads", 0, -1),
     ("token_stride", 3, -1),
     ("tokens_per_frame", 33, 0),       # fine with stride 1
+    ("tokens_per_frame", 8388576, 0),  # largest frame at D = 128: 2 * D * Tv < 2^31
+    ("tokens_per_frame", 8388577, -2), # Tv rounds up to 2^23: one slot reaches 2 GiB
+    ("tokens_per_frame", 2**31 - 1, -2),
     ("window_frames", 2, -2),          # W < C
     ("sink_frames", 60, -2),           # S + W > 64
     ("rot_dim", 129, -1),
