@@ -303,7 +303,8 @@ int fp4kv_rope_rel(const void *x, int in_dtype, void *y, int out_dtype, int64_t 
   if (n_tokens == 0) return FP4KV_OK;
   if (rot_dim > 0 && (long long)pos0 + (n_tokens - 1) / tokens_per_frame >= n_pos)
     return FP4KV_ESHAPE;   // rot_dim 0 reads no table
-  if (n_tokens * n_heads * (long long)head_dim > (1ll << 40)) return FP4KV_ESHAPE;
+  if (n_tokens > (1ll << 40) || n_tokens * n_heads * (long long)head_dim > (1ll << 40))
+    return FP4KV_ESHAPE;
   RopeParams p;
   p.x = x;
   p.y = y;

@@ -239,6 +239,7 @@ def test_rope_validation_before_launch():
     assert call(cs=None) == -1
     assert call(rd=0, cs=None, n=0) == 0   # rot_dim 0 reads no table
     assert call(rd=0, pos0=40, n=0) == 0
+    assert call(rd=0, cs=None, n=2**62) == -2   # too large, rejected before the size product
 
 
 def test_attention_validation_before_launch():
