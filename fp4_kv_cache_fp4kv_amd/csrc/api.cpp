@@ -391,6 +391,10 @@ int fp4kv_attention_chunk(const fp4kv_cache *c, const void *q_rot, int q_dtype, 
       n_wg = n_workgroups;
     }
     n_wg = std::min(n_wg, n_rb * n_v);   // no empty range
+    // Many pieces per row block (at least 4 on average): combine them in a
+    // second kernel spread over the row blocks' 32-row slices instead of in
+    // the one workgroup that finishes a row block last.
+    p.merge_pass = n_wg >= 3 * n_rb;
     if (workspace_bytes < attn_workspace_bytes(c->head_dim, n_wg)) return FP4KV_ESHAPE;
     uint8_t *ws = (uint8_t *)workspace;
     p.ws_cnt = (int32_t *)ws;

@@ -25,7 +25,9 @@
 //     of a later tile in their shadow) the other does the softmax;
 //   * split schedule: the key tiles of all row blocks are cut into one
 //     contiguous range per workgroup; a row block shared by two or more
-//     ranges is finished by a log-sum-exp merge of the pieces.
+//     ranges is finished by a log-sum-exp merge of the pieces, in the
+//     workgroup that completes the row block or, when the row blocks are cut
+//     into many pieces, in a second kernel (merge_kernel).
 //
 // Rotation: the cache holds keys before rotation.  Rotating q by pos(qf) and
 // k by pos(kf) gives the same score as rotating q by pos(qf) - pos(kf), so
@@ -35,8 +37,10 @@
 //
 // Precision: the turned-back queries are split into an f16 high part and an
 // f16 low part (two MFMAs on the same exact key operand), so scores carry
-// about 22 bits; P is rounded to f16 (the row sum adds the unrounded
-// weights).  softmax_scale * log2(e) * g_k (the key
+// about 22 bits; P is rounded to f16 and the row sum adds the same rounded
+// weights, so a row dominated by one key returns that key's value exactly
+// (under the lazy rescale the dominant weight is any value up to 2^8, not
+// 1).  softmax_scale * log2(e) * g_k (the key
 // tensor scale of the frame) multiplies the scores inside the exp2 argument;
 // the value tensor scale is folded into the output accumulator when the frame
 // changes.
@@ -388,9 +392,10 @@ __device__ __forceinline__ void scores(f32x16 (&s)[2], const uint16_t (*kt)[D + 
 // l += sum of P.
 __device__ __forceinline__ void softmax_weights(const f32x16 (&s)[2], float cf, float m,
                                                 float &l, f16x8 (&pb)[4]) {
-  // The row sum adds the float32 weights in 8 independent partial sums (a
-  // packed f16 dot product of the rounded weights is a slow instruction
-  // here and made the whole kernel 7% slower).
+  // The row sum adds the rounded weights, converted back to float32, in 8
+  // independent partial sums (a packed f16 dot product is a slow
+  // instruction here and made the whole kernel 7% slower; a mixed-precision
+  // FMA per weight made the compiler spill 89 registers).
   float lp[2][4] = {};
 #pragma unroll
   for (int b = 0; b < 2; ++b)
@@ -402,7 +407,7 @@ __device__ __forceinline__ void softmax_weights(const f32x16 (&s)[2], float cf, 
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b][8 * t2 + 2 * e], cf, -m));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b][8 * t2 + 2 * e + 1], cf, -m));
         const f16x2 ph = {(_Float16)p0, (_Float16)p1};
-        lp[b][e] += p0 + p1;
+        lp[b][e] += (float)ph[0] + (float)ph[1];
         w[e] = bits(ph);
       }
       pb[2 * b + t2] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
@@ -517,6 +522,12 @@ __device__ __forceinline__ long long split_start(int w, long long n_units, int n
   return (long long)w * n_units / n_wg;
 }
 
+// One log-sum-exp merge step, a_old * acc + a_in * x, with one rounding
+// order fixed for both merge paths.
+__device__ __forceinline__ float merge_step(float acc, float a_old, float x, float a_in) {
+  return fmaf(x, a_in, acc * a_old);
+}
+
 // Workgroup whose range holds virtual tile x: the largest w with
 // split_start(w) <= x.
 __device__ __forceinline__ int split_owner(long long x, long long n_units, int n_wg) {
@@ -568,7 +579,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
   // lies inside one range is finished directly; the pieces of a row block
   // shared by several ranges leave partial results (g_v * acc, m, l) in the
   // workspace, and the workgroup that completes the row block last merges
-  // them.  Workgroups are dispatched round-robin over the 8 XCDs (each with
+  // them (with a merge pass, merge_kernel does).  Workgroups are dispatched round-robin over the 8 XCDs (each with
   // its own L2): XCD x takes the contiguous ranges of workgroups
   // [x*per, (x+1)*per), so each head's FP4 KV is read into few L2s.
   const int per = (int)gridDim.x / kXcds;
@@ -930,6 +941,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
         __builtin_amdgcn_raw_buffer_store_b64(ml, ws_ml, (slot * kBM + row) * 8, 0, kSc1);
       }
     }
+    if (p.merge_pass) continue;   // merge_kernel combines the pieces
     const int w_first = split_owner(vbase, n_units, p.n_wg);
     const int w_last = split_owner(vbase + n_v - 1, n_units, p.n_wg);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the piece is written
@@ -958,7 +970,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
       const float a_old = __builtin_amdgcn_exp2f(m_all - m_new);
       const float a_in = __builtin_amdgcn_exp2f(m_in - m_new);
       m_all = m_new;
-      l_all = l_all * a_old + l_in * a_in;
+      l_all = merge_step(l_all, a_old, l_in, a_in);
       const int ib = ((slot * kBM + row) * D + 4 * hf) * 4;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -968,10 +980,93 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
               __builtin_amdgcn_raw_buffer_load_b128(ws_o, ib + (32 * db + 8 * i) * 4, 0, kSc1);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            oacc[db][4 * i + e] = oacc[db][4 * i + e] * a_old + __uint_as_float(x[e]) * a_in;
+            oacc[db][4 * i + e] =
+                merge_step(oacc[db][4 * i + e], a_old, __uint_as_float(x[e]), a_in);
         }
     }
     store_out(l_all > 0.0f ? __fdiv_rn(1.0f, l_all) : 0.0f);
+  }
+}
+
+// Merge pass of the split schedule, for calls whose row blocks are cut into
+// many pieces: the pieces of a row block are combined by 8 workgroups (one
+// per 32-row slice, one wave per 32-dimension block) instead of by the one
+// workgroup that finishes last.  The arithmetic per output element is the
+// in-kernel merge's, in the same workgroup order; up to 8 pieces' loads are
+// in flight at once.  Row blocks finished inside one range are skipped.
+constexpr int kMergeSlices = kBM / 32;
+constexpr int kMergeBatch = 8;
+
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(64 * (D / 32)) void merge_kernel(AttnParams p) {
+  const int n_qt = (p.Nq + kBM - 1) / kBM;
+  const int n_tiles = (p.Tc + kBN - 1) / kBN;
+  const long long n_v = (long long)p.n_slots * n_tiles;
+  const long long n_units = (long long)n_qt * p.H * n_v;
+  const int rb = (int)blockIdx.x / kMergeSlices, slice = (int)blockIdx.x % kMergeSlices;
+  const long long vbase = (long long)rb * n_v;
+  const int w_first = split_owner(vbase, n_units, p.n_wg);
+  const int w_last = split_owner(vbase + n_v - 1, n_units, p.n_wg);
+  if (w_first == w_last) return;   // finished by its one workgroup
+  const int db = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+  const int n = lane & 31, hf = lane >> 5;
+  const int row = slice * 32 + n;   // row within the row block
+  const int head = rb / n_qt;
+  const int my_row = (rb - head * n_qt) * kBM + row;
+  if (my_row >= p.Nq) return;
+  const __amdgpu_buffer_rsrc_t ws_o =
+      rsrc((const uint8_t *)p.ws_o, (uint32_t)(2 * p.n_wg * kBM * D * 4));
+  const __amdgpu_buffer_rsrc_t ws_ml =
+      rsrc((const uint8_t *)p.ws_ml, (uint32_t)(2 * p.n_wg * kBM * 8));
+  float m_all = -1.0e30f, l_all = 0.0f;
+  float acc[16] = {};
+  for (int w0 = w_first; w0 <= w_last; w0 += kMergeBatch) {
+    u32x2 ml[kMergeBatch];
+    u32x4 x[kMergeBatch][4];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const int wc = w0 + k;
+      if (wc <= w_last) {
+        const int slot = 2 * wc + (split_start(wc, n_units, p.n_wg) < vbase ? 1 : 0);
+        ml[k] = __builtin_amdgcn_raw_buffer_load_b64(ws_ml, (slot * kBM + row) * 8, 0, kSc1);
+        const int ib = ((slot * kBM + row) * D + 4 * hf) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          x[k][i] =
+              __builtin_amdgcn_raw_buffer_load_b128(ws_o, ib + (32 * db + 8 * i) * 4, 0, kSc1);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      if (w0 + k <= w_last) {
+        const float m_in = __uint_as_float(ml[k][0]), l_in = __uint_as_float(ml[k][1]);
+        const float m_new = fmaxf(m_all, m_in);
+        const float a_old = __builtin_amdgcn_exp2f(m_all - m_new);
+        const float a_in = __builtin_amdgcn_exp2f(m_in - m_new);
+        m_all = m_new;
+        l_all = merge_step(l_all, a_old, l_in, a_in);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[4 * i + e] = merge_step(acc[4 * i + e], a_old, __uint_as_float(x[k][i][e]), a_in);
+      }
+    }
+  }
+  const float inv = l_all > 0.0f ? __fdiv_rn(1.0f, l_all) : 0.0f;
+  const long long obase = ((long long)my_row * p.H + head) * D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int d = 32 * db + 8 * i + 4 * hf;
+    const float v0 = acc[4 * i] * inv, v1 = acc[4 * i + 1] * inv;
+    const float v2 = acc[4 * i + 2] * inv, v3 = acc[4 * i + 3] * inv;
+    if (OUT_F32) {
+      *(float4 *)((float *)p.o + obase + d) = make_float4(v0, v1, v2, v3);
+    } else {
+      const uint32_t w0 = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+      const uint32_t w1 = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
+      *(uint2 *)((uint16_t *)p.o + obase + d) = make_uint2(w0, w1);
+    }
   }
 }
 
@@ -984,6 +1079,12 @@ hipError_t launch_one(const AttnParams &p, hipStream_t s) {
   if (attr != hipSuccess) return attr;
   const dim3 grid((unsigned)((p.n_wg + kXcds - 1) / kXcds * kXcds));
   hipLaunchKernelGGL((attention_kernel<D, OUT_F32, BF16KV>), grid, dim3(kThreads), bytes, s, p);
+  if (!p.merge_pass) return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long n_rb = (long long)(p.Nq + kBM - 1) / kBM * p.H;
+  hipLaunchKernelGGL((merge_kernel<D, OUT_F32>), dim3((unsigned)(n_rb * kMergeSlices)),
+                     dim3(64 * (D / 32)), 0, s, p);
   return hipGetLastError();
 }
 

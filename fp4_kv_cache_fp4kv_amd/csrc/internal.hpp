@@ -73,6 +73,7 @@ struct AttnParams {
   float *ws_o;             // partial g_v * acc [2 n_wg][256 rows][D]
   float2 *ws_ml;           // partial (m, l) [2 n_wg][256 rows]
   int *ws_cnt;             // pieces counted in per row block [n_wg], zero between launches
+  int merge_pass;          // pieces of cut row blocks are combined by merge_kernel
   int32_t q_shot[FP4KV_MAX_FRAMES];
 };
 

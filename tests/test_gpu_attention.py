@@ -141,7 +141,9 @@ def test_attention_empty_cache_gives_zeros():
 
 # 4 row blocks of 300 rows x 2 heads, 14 key tiles each at a full window
 # (7 slots x 2 tiles, the second ragged): 1 workgroup takes every row block
-# whole; 3, 5 and 13 workgroups cut row blocks into 2 to 4 merged pieces.
+# whole; 3, 5 and 13 workgroups cut row blocks into 2 to 4 merged pieces,
+# merged by the workgroup that finishes a row block (3, 5) or, at 3 or more
+# workgroups per row block, by the separate merge kernel (13).
 @pytest.mark.parametrize("n_wg", [1, 3, 5, 13])
 def test_attention_split_schedules(n_wg):
     w = wl.Workload("split", H=2, D=128, T=100, C=3, S=1, W=6, n_frames=15, seed=24,
@@ -156,11 +158,32 @@ def test_attention_without_workspace():
     _run_stream(w, [1, 4], split=False)
 
 
-@pytest.mark.parametrize("n_wg", [2, 7])
+@pytest.mark.parametrize("n_wg", [2, 7, 13])   # 13: merge kernel (3 row blocks)
 def test_attention_split_multishot_d64(n_wg):
     w = wl.Workload("tiny_mix", H=3, D=64, T=24, C=3, S=2, W=6, n_frames=20, seed=21,
                     dtype="bf16", token_stride=2, shot_len=5)
     _run_stream(w, list(range(w.n_chunks)), n_wg=n_wg)
+
+
+@pytest.mark.parametrize("n_wg", [5, 13])
+def test_attention_split_bf16_output(n_wg):
+    """bf16 output of a split call, merged in the workgroup that finishes a
+    row block (5) or by the merge kernel (13): the float32 output rounded
+    once, and the float32 output within the bar."""
+    from fp4_kv_cache_fp4kv_amd import api
+    w = wl.Workload("split", H=2, D=128, T=100, C=3, S=1, W=6, n_frames=15, seed=24,
+                    outlier_p=0.01, outlier_scale=20.0)
+    gc, oc = gpu_cache(w), OracleCache.for_workload(w)
+    for c in range(3):
+        f0, n = w.chunk_frames(c)
+        (q, qb), (k, kb), (v, vb) = step_inputs(w, c)
+        oc.append(k, v, f0, n, [0] * n)
+        o32 = _gpu_step(api, gc, w, c, q, qb, k, kb, v, vb, n_wg=n_wg)
+        o16 = _gpu_step(api, gc, w, c, q, qb, k, kb, v, vb, out_dtype=torch.bfloat16,
+                        append=False, n_wg=n_wg)
+        assert np.all(np.abs(o16 - o32) <= np.abs(o32) * 2.0 ** -8 + 1e-30)
+        mx, mn = err_stats(o32, oc.attention(q, f0, n, [0] * n))
+        assert mx <= MAX_ABS and mn <= MEAN_ABS
 
 
 def test_attention_split_is_deterministic():
