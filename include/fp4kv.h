@@ -351,7 +351,10 @@ int fp4kv_rope_rel(const void *x, int in_dtype, void *y, int out_dtype, int64_t 
  * Work split: the key tiles of all (256-row block, head) pairs are cut into
  * one contiguous range per workgroup.  A row block shared by two or more
  * ranges is merged from partial results (log-sum-exp combine, in a fixed
- * order, so repeated calls give identical bytes) kept in the workspace.
+ * order, so repeated calls give identical bytes) kept in the workspace: by
+ * the workgroup that completes the row block, or, when there are at least
+ * 3 workgroups per row block, by a second kernel enqueued on the same stream
+ * right after the first.
  *   n_workgroups  0: one workgroup per compute unit of the current device
  *                 (each range at least 4 key tiles); n > 0: n workgroups
  *                 (at most FP4KV_MAX_WORKGROUPS).  With workspace == NULL
