@@ -148,7 +148,7 @@ def test_attention_empty_cache_gives_zeros():
 def test_attention_split_schedules(n_wg):
     w = wl.Workload("split", H=2, D=128, T=100, C=3, S=1, W=6, n_frames=15, seed=24,
                     outlier_p=0.01, outlier_scale=20.0)
-    _run_stream(w, [1, 4], n_wg=n_wg)
+    _run_stream(w, list(range(w.n_chunks)), n_wg=n_wg)
 
 
 def test_attention_without_workspace():
