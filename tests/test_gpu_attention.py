@@ -229,6 +229,13 @@ def test_attention_full_size_sampled(name):
     _run_stream(w, steps, rows=_sample_rows(w), heads=[0, w.H // 2, w.H - 1])
 
 
+def test_attention_full_size_all_rows():
+    """Every query row of two heads of the 1.3B-like layer (1% outliers x20)
+    at its first full-window step."""
+    w = wl.L13B
+    _run_stream(w, [(w.S + w.W) // w.C - 1], heads=[0, w.H - 1])
+
+
 def test_attention_full_size_without_workspace():
     """5B-like layer with one workgroup per row block (264 of them: a
     second round on 256 CUs)."""
