@@ -3,8 +3,9 @@
 This module is shared by the tests, the benchmark and the CPU oracle's
 callers.  It holds no step of the method: only layer shapes, stream
 schedules and seeded random tensors.  The shapes stand in for the 1.3B and
-5B causal video generators the LongLive 2.0 pages describe (page 5, "Model
-Range and Hardware Requirements"); no dataset or checkpoint is involved.
+5B causal video generators the LongLive 2.0 pages describe (evermx.com,
+"Model Range and Hardware Requirements"); no dataset or checkpoint is
+involved.
 
 Random draws: for workload seed s, chunk step k and tensor id (Q=0, K=1,
 V=2) the generator is ``numpy.random.default_rng(SeedSequence([s, k, id]))``.

@@ -41,10 +41,13 @@ def rotate(x, pos, rot_dim: int, base: float = 10000.0) -> np.ndarray:
 # ------------------------------------------------ float32 rotation (stored keys)
 # Where a rotation feeds the NVFP4 encoder (keys rotated before they are
 # stored, and their re-rotation when the window slides) the rotated value
-# decides codes, so its arithmetic is fixed exactly.  The pages give no
-# precision; the reading taken is the kernel's: a float32 cos/sin table
-# evaluated in float64 and rounded once, and each product rounded to float32
-# before the sum is rounded (no fused multiply-add).
+# decides codes, so its arithmetic must be fixed exactly.  The pages give no
+# precision.  Reading: the rotation formula evaluated in IEEE float32 as
+# written, one correctly rounded operation at a time -- the two products,
+# then their difference or sum -- with the cos/sin table entries evaluated in
+# float64 and rounded once to float32.  This is the plain float32 evaluation
+# of the formula (no operation fused), which any float32 implementation can
+# reproduce exactly.
 
 def table_f32(n_pos: int, rot_dim: int, base: float = 10000.0) -> np.ndarray:
     """float32 [n_pos][rot_dim/2][2]: (cos, sin) of pos * base^(-2i/rot_dim),

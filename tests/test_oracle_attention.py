@@ -157,26 +157,45 @@ def test_shot_mask_equals_filtered_key_set_and_reduces_to_single_shot():
                     dtype="f32", shot_len=4)
     single = wl.Workload("tiny_1", H=1, D=64, T=16, C=3, S=1, W=6, n_frames=14, seed=9,
                          dtype="f32", shot_len=100)
+    plain = wl.Workload("tiny_0", H=1, D=64, T=16, C=3, S=1, W=6, n_frames=14, seed=9,
+                        dtype="f32")
     cs, c1 = OracleCache.for_workload(w), OracleCache.for_workload(single)
+    c0 = OracleCache.for_workload(plain)
     for c in range(w.n_chunks):
         f0, n = w.chunk_frames(c)
         q, k, v = _stream_inputs(w, c)
         shots = [w.shot_of(f) for f in range(f0, f0 + n)]
         cs.append(k, v, f0, n, shots)
-        c1.append(k, v, f0, n, [single.shot_of(f) for f in range(f0, f0 + n)])
+        # one shot that outlasts the stream, labelled 7 on every frame
+        long_shot = [single.shot_of(f) + 7 for f in range(f0, f0 + n)]
+        c1.append(k, v, f0, n, long_shot)
+        c0.append(k, v, f0, n, [plain.shot_of(f) for f in range(f0, f0 + n)])
         out = cs.attention(q, f0, n, shots)
         f1 = f0 + n
         # per query frame: SDPA on a single-shot cache restricted to sink + same shot
-        o1 = c1.attention(q, f0, n, [0] * n)
+        o1 = c1.attention(q, f0, n, long_shot)
         for a, qf in enumerate(range(f0, f1)):
             rows = slice(a * w.T, (a + 1) * w.T)
             same = all(w.shot_of(kf) == w.shot_of(qf) or kf < w.S
                        for kf in ring.visible_frames(f1, w.S, w.W) if kf // w.C <= qf // w.C)
             if same:
                 assert np.allclose(out[rows], o1[rows], atol=1e-12)
-        # shot_len >= F reduces to single shot
-        o_big = c1.attention(q, f0, n, [0] * n)
-        assert np.array_equal(o_big, o1)
+        # shot_len >= F reduces to single shot: the cache fed one long shot
+        # (id 7) attends exactly like the cache of the shot-free workload
+        # (id 0), and like SDPA over every visible key with no shot filter
+        o_plain = c0.attention(q, f0, n, [0] * n)
+        assert np.array_equal(o1, o_plain)
+        keys = [(s, kf) for s, kf in c0.visible_slots(f1)]
+        K = np.concatenate([c0.decode_slot(s)[0][0] for s, _ in keys])
+        V = np.concatenate([c0.decode_slot(s)[1][0] for s, _ in keys])
+        kp = np.concatenate([np.full(w.T, ring.rel_pos(kf, f1, w.S, w.W)) for _, kf in keys])
+        kchunk = np.concatenate([np.full(w.T, kf // w.C) for _, kf in keys])
+        for a, qf in enumerate(range(f0, f1)):
+            rows = slice(a * w.T, (a + 1) * w.T)
+            mask = np.tile(kchunk <= qf // w.C, (w.T, 1))
+            qp = np.full(w.T, ring.rel_pos(qf, f1, w.S, w.W))
+            ref = _sdpa(rope.rotate(q[rows, 0], qp, w.D), rope.rotate(K, kp, w.D), V, mask)
+            assert np.allclose(o1[rows, 0], ref, atol=1e-12)
     # explicit filter check on the last step
     f0, n = w.chunk_frames(w.n_chunks - 1)
     q, _, _ = _stream_inputs(w, w.n_chunks - 1)

@@ -4,7 +4,9 @@ when the window start moves), against facts that do not come from the
 oracle's own formulas:
 
   * the float32 rotary table against float64 cos/sin, and the float32
-    rotation against the float64 rotation (rounding bounds);
+    rotation against the float64 rotation (rounding bounds), against exact
+    rational arithmetic with one float32 rounding per operation, and against
+    torch's float32 elementwise ops (bit for bit);
   * quarter turns are exact in float32 and commute with NVFP4 encoding when
     every frame carries the same planted maximum 2688 * 2^-6 (tensor scale
     2^-6 exactly, so re-encoding is lossless): the stored keys must then be
@@ -51,6 +53,73 @@ def test_rotate_f32_close_to_float64_rotation():
     yi = rope.rotate_f32(x, t[pos][:, None], inverse=True)
     refi = rope.rotate(x, -pos[:, None], 48)
     assert np.all(np.abs(yi[..., :48] - refi[..., :48]) <= bound)
+
+
+def _rne_f32(r):
+    """The float32 nearest to the rational r (ties to even), from exact
+    integer arithmetic: one correctly rounded IEEE binary32 operation."""
+    from fractions import Fraction
+    if r == 0:
+        return np.float32(0.0)
+    sign = -1 if r < 0 else 1
+    a = abs(Fraction(r))
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # 2^e <= a < 2^(e+2)
+    if a < Fraction(2) ** e:
+        e -= 1
+    if a >= Fraction(2) ** (e + 1):
+        e += 1
+    q = max(e, -126) - 23                                      # quantum of the binade
+    m = a / Fraction(2) ** q
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return np.float32(sign * float(Fraction(fl) * Fraction(2) ** q))
+
+
+def test_rotate_f32_is_one_rounding_per_operation():
+    """rotate_f32 pinned to the formula evaluated with exact rational
+    arithmetic and one float32 rounding after each product and after the
+    sum, and to torch's float32 elementwise ops on the CPU (a library
+    routine; separate ops, so nothing is fused): bit for bit on values that
+    include cancellation, tiny products and large magnitudes."""
+    import torch
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    n = 600
+    a = rng.standard_normal(n).astype(np.float32)
+    b = rng.standard_normal(n).astype(np.float32)
+    a[:100] *= np.float32(2.0 ** -60)                   # products near the subnormal range
+    b[100:200] = a[100:200] * np.float32(1.0 + 2.0 ** -20)   # near cancellation
+    a[200:300] *= np.float32(3.0e4)
+    t = rope.table_f32(64, 2)                            # pair 0 turns by pos radians
+    pos = rng.integers(0, 64, size=n)
+    cs = t[pos]                                          # [n][1][2]
+    x = np.stack([a, b], axis=-1)                        # [n][2]
+    for inverse in (False, True):
+        got = rope.rotate_f32(x, cs, inverse=inverse)
+        c = cs[:, 0, 0]
+        sn = -cs[:, 0, 1] if inverse else cs[:, 0, 1]
+        F = Fraction
+        want0 = [_rne_f32(F(float(_rne_f32(F(float(ai)) * F(float(ci))))) -
+                          F(float(_rne_f32(F(float(bi)) * F(float(si))))))
+                 for ai, bi, ci, si in zip(a, b, c, sn)]
+        want1 = [_rne_f32(F(float(_rne_f32(F(float(ai)) * F(float(si))))) +
+                          F(float(_rne_f32(F(float(bi)) * F(float(ci))))))
+                 for ai, bi, ci, si in zip(a, b, c, sn)]
+        want = np.stack([np.array(want0, np.float32), np.array(want1, np.float32)], axis=-1)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+        ta, tb = torch.from_numpy(a), torch.from_numpy(b)
+        tc, ts = torch.from_numpy(np.ascontiguousarray(c)), torch.from_numpy(np.ascontiguousarray(sn))
+        t0 = torch.sub(torch.mul(ta, tc), torch.mul(tb, ts))
+        t1 = torch.add(torch.mul(ta, ts), torch.mul(tb, tc))
+        tw = torch.stack([t0, t1], dim=-1).numpy()
+        assert np.array_equal(got.view(np.uint32), tw.view(np.uint32))
+    # the pin catches a fused multiply-add (one rounding for a*c - b*s)
+    fused = [_rne_f32(F(float(ai)) * F(float(ci)) - F(float(_rne_f32(F(float(bi)) * F(float(si))))))
+             for ai, bi, ci, si in zip(a, b, cs[:, 0, 0], cs[:, 0, 1])]
+    got = rope.rotate_f32(x, cs)
+    assert not np.array_equal(got[:, 0].view(np.uint32), np.array(fused, np.float32).view(np.uint32))
 
 
 def _quarter_table(n_pos, half):
