@@ -594,7 +594,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
   for (long long blk = blk0; blk * n_v < u1; ++blk) {
     const long long vbase = blk * n_v;
     const int v_lo = (int)(max(u0, vbase) - vbase), v_hi = (int)(min(u1, vbase + n_v) - vbase);
-    if (blk != blk0) __syncthreads();   // the previous row block's LDS is no longer read
+    // Every wave has finished reading the previous row block's frame list,
+    // turn table and tiles once it passes this barrier.  (The first row
+    // block needs none; the barrier is unconditional so that the protocol
+    // does not depend on the order in which row blocks are visited.)
+    __syncthreads();
     // The kernel arguments and the thread index are made opaque in every
     // segment, so that the compiler derives addresses and divisors here
     // instead of holding them (spilled) across the segment loop.
