@@ -29,7 +29,8 @@ FP4KV_MAX_SLOTS = 64
 EXPORTED = ("fp4kv_strerror", "fp4kv_abi_version", "fp4kv_cache_nbytes", "fp4kv_cache_reset",
             "fp4kv_append_workspace_bytes", "fp4kv_quantize_append", "fp4kv_rope_table",
             "fp4kv_rope_rel", "fp4kv_attention_chunk", "fp4kv_attention_workspace_bytes",
-            "fp4kv_rerotate_window", "fp4kv_quantize_append_rotated")
+            "fp4kv_rerotate_window", "fp4kv_quantize_append_rotated",
+            "fp4kv_quantize_append_noalloc")
 
 
 class CacheDesc(ctypes.Structure):
@@ -91,6 +92,9 @@ def load() -> ctypes.CDLL:
                                           P(c_i32),
                                           vp, vp, ctypes.c_size_t, vp]
     lib.fp4kv_quantize_append.restype = c_int
+    lib.fp4kv_quantize_append_noalloc.argtypes = [P(CacheDesc), vp, vp, c_int, c_i32, c_i32,
+                                                  P(c_i32), P(c_i32), vp, vp]
+    lib.fp4kv_quantize_append_noalloc.restype = c_int
     lib.fp4kv_rerotate_window.argtypes = [P(CacheDesc), c_i32, c_i32, vp, c_i32, vp,
                                           ctypes.c_size_t, vp]
     lib.fp4kv_rerotate_window.restype = c_int

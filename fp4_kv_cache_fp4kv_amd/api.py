@@ -156,6 +156,30 @@ def quantize_append(cache: FP4KVCache, k: torch.Tensor, v: torch.Tensor, frame0:
     check(st, "fp4kv_quantize_append")
 
 
+def quantize_append_noalloc(cache: FP4KVCache, k: torch.Tensor, v: torch.Tensor, frame0: int,
+                            n_frames: int, shots: Sequence[int],
+                            tscale: Optional[torch.Tensor] = None,
+                            shot_starts: Optional[Sequence[int]] = None) -> None:
+    """fp4kv_quantize_append_noalloc on the current stream: the same append
+    with the library's own per-device workspace (no caller workspace, no
+    allocation)."""
+    for t, nm in ((k, "k"), (v, "v")):
+        _require(t, nm, device=cache.device)
+    if k.dtype != v.dtype or k.dtype not in _DTYPES:
+        raise ValueError("k and v must both be float32 or bfloat16")
+    if k.shape != (n_frames * cache.T, cache.H, cache.D) or v.shape != k.shape:
+        raise ValueError(f"k/v must have shape {(n_frames * cache.T, cache.H, cache.D)}")
+    if len(shots) != n_frames:
+        raise ValueError("one shot id per frame")
+    if tscale is not None:
+        _require(tscale, "tscale", torch.float32, cache.device)
+    st = load().fp4kv_quantize_append_noalloc(
+        ctypes.byref(cache.desc), k.data_ptr(), v.data_ptr(), _DTYPES[k.dtype], frame0, n_frames,
+        _i32_array(shots), None if shot_starts is None else _i32_array(shot_starts),
+        _ptr(tscale), _stream(cache.device))
+    check(st, "fp4kv_quantize_append_noalloc")
+
+
 def quantize_append_rotated(cache: FP4KVCache, k: torch.Tensor, v: torch.Tensor, frame0: int,
                             n_frames: int, shots: Sequence[int],
                             tscale: Optional[torch.Tensor] = None,

@@ -14,7 +14,7 @@ using namespace fp4kv;
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -71,6 +71,21 @@ int check_buffers(const fp4kv_cache *c) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? FP4KV_OK : FP4KV_EDEVICE; }
 
+// Workspace fields of the codec's parameters.
+void set_append_ws(AppendParams &p, void *workspace) {
+  p.ws_partial = (uint32_t *)workspace;
+  p.ws_rr = (uint32_t *)workspace + kWsRrOffset;
+  p.ws_rr_g = (float *)((uint32_t *)workspace + kWsRrGOffset);
+}
+
+// Caller workspace of an append: present, large enough, aligned.
+int check_append_ws(const void *workspace, size_t workspace_bytes) {
+  if (!workspace) return FP4KV_EINVAL;
+  if (workspace_bytes < kWsBytes) return FP4KV_ESHAPE;
+  if (!aligned16(workspace)) return FP4KV_EALIGN;
+  return FP4KV_OK;
+}
+
 // Cache fields of the codec's parameters; no frames, no window move.
 void fill_append(AppendParams &p, const fp4kv_cache *c, void *workspace) {
   memset(&p, 0, sizeof(p));
@@ -82,9 +97,7 @@ void fill_append(AppendParams &p, const fp4kv_cache *c, void *workspace) {
   p.tscale[1] = c->v_tscale;
   p.slot_frame = c->slot_frame;
   p.slot_shot = c->slot_shot;
-  p.ws_partial = (uint32_t *)workspace;
-  p.ws_rr = (uint32_t *)workspace + kWsRrOffset;
-  p.ws_rr_g = (float *)((uint32_t *)workspace + kWsRrGOffset);
+  set_append_ws(p, workspace);
   p.H = c->n_heads;
   p.D = c->head_dim;
   p.T = c->tokens_per_frame;
@@ -99,14 +112,14 @@ void fill_append(AppendParams &p, const fp4kv_cache *c, void *workspace) {
 }
 
 // Validation and parameters shared by the appends (nothing enqueued).
+// The workspace is checked and set by the caller (set_append_ws).
 int prepare_append(AppendParams &p, const fp4kv_cache *c, const void *k, const void *v,
                    int in_dtype, int32_t frame0, int32_t n_frames, const int32_t *frame_shot,
-                   const int32_t *frame_shot_start, const float *tscale_in, void *workspace,
-                   size_t workspace_bytes) {
+                   const int32_t *frame_shot_start, const float *tscale_in) {
   int st = check_shape(c);
   if (st) return st;
   if ((st = check_buffers(c))) return st;
-  if (!k || !v || !frame_shot || !workspace) return FP4KV_EINVAL;
+  if (!k || !v || !frame_shot) return FP4KV_EINVAL;
   if (in_dtype != FP4KV_F32 && in_dtype != FP4KV_BF16) return FP4KV_EINVAL;
   if (frame0 < 0 || n_frames < 1 || n_frames > FP4KV_MAX_FRAMES) return FP4KV_EINVAL;
   if (c->sink_per_shot && !frame_shot_start) return FP4KV_EINVAL;
@@ -128,11 +141,10 @@ int prepare_append(AppendParams &p, const fp4kv_cache *c, const void *k, const v
     }
   }
   if ((long long)frame0 + n_frames > (1ll << 30)) return FP4KV_EINVAL;
-  if (workspace_bytes < kWsBytes) return FP4KV_ESHAPE;
-  if (!aligned16(k) || !aligned16(v) || !aligned16(workspace)) return FP4KV_EALIGN;
+  if (!aligned16(k) || !aligned16(v)) return FP4KV_EALIGN;
   if (tscale_in && ((uintptr_t)tscale_in & 3u)) return FP4KV_EALIGN;
 
-  fill_append(p, c, workspace);
+  fill_append(p, c, nullptr);
   p.x[0] = k;
   p.x[1] = v;
   p.tscale_in = tscale_in;
@@ -223,8 +235,26 @@ int fp4kv_quantize_append(const fp4kv_cache *c, const void *k, const void *v, in
                           void *workspace, size_t workspace_bytes, void *stream) {
   AppendParams p;
   int st = prepare_append(p, c, k, v, in_dtype, frame0, n_frames, frame_shot, frame_shot_start,
-                          tscale_in, workspace, workspace_bytes);
+                          tscale_in);
   if (st) return st;
+  if ((st = check_append_ws(workspace, workspace_bytes))) return st;
+  set_append_ws(p, workspace);
+  return from_hip(launch_append(p, (hipStream_t)stream));
+}
+
+int fp4kv_quantize_append_noalloc(const fp4kv_cache *c, const void *k, const void *v,
+                                  int in_dtype, int32_t frame0, int32_t n_frames,
+                                  const int32_t *frame_shot, const int32_t *frame_shot_start,
+                                  const float *tscale_in, void *stream) {
+  AppendParams p;
+  int st = prepare_append(p, c, k, v, in_dtype, frame0, n_frames, frame_shot, frame_shot_start,
+                          tscale_in);
+  if (st) return st;
+  void *ws = nullptr;
+  size_t ws_bytes = 0;
+  if (append_scratch(&ws, &ws_bytes) != hipSuccess) return FP4KV_EDEVICE;
+  if ((st = check_append_ws(ws, ws_bytes))) return st;   // the array's fixed size
+  set_append_ws(p, ws);
   return from_hip(launch_append(p, (hipStream_t)stream));
 }
 
@@ -236,8 +266,10 @@ int fp4kv_quantize_append_rotated(const fp4kv_cache *c, const void *k, const voi
                                   size_t workspace_bytes, void *stream) {
   AppendParams p;
   int st = prepare_append(p, c, k, v, in_dtype, frame0, n_frames, frame_shot, frame_shot_start,
-                          tscale_in, workspace, workspace_bytes);
+                          tscale_in);
   if (st) return st;
+  if ((st = check_append_ws(workspace, workspace_bytes))) return st;
+  set_append_ws(p, workspace);
   if (!keys_rotated(c)) return FP4KV_EINVAL;
   if (f1_prev < 0 || f1 < f1_prev || f1 > (1 << 30) || (long long)frame0 + n_frames > f1)
     return FP4KV_EINVAL;

@@ -11,6 +11,8 @@
 // the same ring layout.  For caches that store keys rotated, the same two
 // kernels also turn the appended keys by their positions and re-encode the
 // window slots a window move turns (grid rows / workgroups of their own).
+#include <mutex>
+
 #include "fp4kv_device.hpp"
 #include "internal.hpp"
 
@@ -498,6 +500,41 @@ __global__ void reset_kernel(int32_t *slot_frame, int32_t *slot_shot, float *kt,
 }
 
 }  // namespace
+
+// ---- append workspace for callers that cannot allocate ----
+// fp4kv_quantize_append_noalloc keeps the append's workspace (partial maxima
+// between its two kernels) in this array instead of a caller buffer.  Each
+// device holds its own copy for the life of the process; every call on a
+// device shares it, so calls that overlap in time on one device race.  No
+// part of it needs clearing: the amax kernel writes every partial maximum
+// the encode kernel reads.
+static __device__ __align__(256) uint8_t scratch[kWsBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+}  // namespace
+
+hipError_t append_scratch(void **out, size_t *bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    // once per device, with that device current: the host-side name of the
+    // array is not a device address, so only this pointer is ever used
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  *bytes = sizeof(scratch);
+  return hipSuccess;
+}
 
 hipError_t launch_cache_reset(const fp4kv_cache &c, hipStream_t s) {
   const int n = c.sink_frames + c.window_frames;

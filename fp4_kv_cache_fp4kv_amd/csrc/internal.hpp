@@ -79,6 +79,9 @@ struct AttnParams {
 
 hipError_t launch_cache_reset(const fp4kv_cache &c, hipStream_t s);
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
+// Device address and size of the library's own append workspace on the
+// current device (resolved once per device).
+hipError_t append_scratch(void **out, size_t *bytes);
 hipError_t launch_rope(const RopeParams &p, hipStream_t s);
 hipError_t launch_attention(const AttnParams &p, int head_dim, int out_f32, hipStream_t s);
 

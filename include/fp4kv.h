@@ -30,7 +30,8 @@
  *     synchronization.
  *   - Tensors are dense, row-major, with the innermost dimension last.
  *   - Inputs must be finite; NaN and Inf inputs give unspecified codes.
- *   - The library keeps no mutable global state, so calls on different
+ *   - The library keeps no mutable global state, except the per-device
+ *     workspace of fp4kv_quantize_append_noalloc, so calls on different
  *     streams and caches may run concurrently.  Calls that touch the same
  *     cache buffers must be ordered by the caller (same stream or events).
  */
@@ -222,6 +223,25 @@ int fp4kv_quantize_append(const fp4kv_cache *c, const void *k, const void *v,
                           const int32_t *frame_shot, const int32_t *frame_shot_start,
                           const float *tscale_in, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/*
+ * fp4kv_quantize_append_noalloc - fp4kv_quantize_append without a caller
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments, encoding, results and errors are those of
+ * fp4kv_quantize_append; the workspace is a fixed array of
+ * fp4kv_append_workspace_bytes() bytes that the library keeps in device
+ * memory, one per device, for the life of the process (resolved on the first
+ * call on each device).  The call allocates nothing.  All calls on one device
+ * share that array: calls that overlap in time on one device race and must
+ * be ordered by the caller (same stream or events).  No input size changes
+ * the workspace it needs.  FP4KV_EDEVICE if the array's device address cannot
+ * be obtained.
+ */
+int fp4kv_quantize_append_noalloc(const fp4kv_cache *c, const void *k, const void *v,
+                                  int in_dtype, int32_t frame0, int32_t n_frames,
+                                  const int32_t *frame_shot, const int32_t *frame_shot_start,
+                                  const float *tscale_in, void *stream);
 
 /*
  * fp4kv_quantize_append_rotated - the cache update of a

@@ -58,7 +58,7 @@ def _desc(**kw):
 
 def test_strerror_and_version():
     lib = _lib.load()
-    assert lib.fp4kv_abi_version() == 3
+    assert lib.fp4kv_abi_version() == 4
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.fp4kv_strerror(st)
     assert lib.fp4kv_append_workspace_bytes() >= 64 * 33 * 4   # re-rotation maxima
@@ -218,6 +218,29 @@ def test_append_validation_before_launch():
     assert call(c=bad) == -3
     bad.k_codes = 0
     assert call(c=bad) == -1
+
+
+def test_append_noalloc_validation_before_launch():
+    """The no-alloc append validates like the workspace append, before it
+    touches the device (only invalid calls here: a valid one would launch)."""
+    lib = _lib.load()
+    c = _desc()
+    shots = (ctypes.c_int32 * 4)(0, 0, 0, 0)
+    A = 0x100000
+    call = lambda **kw: lib.fp4kv_quantize_append_noalloc(
+        ctypes.byref(kw.get("c", c)), kw.get("k", A), kw.get("v", A), kw.get("dt", 1),
+        kw.get("f0", 0), kw.get("n", 3), kw.get("shots", shots), kw.get("starts", None),
+        kw.get("ts", None), None)
+    assert call(k=None) == -1
+    assert call(dt=7) == -1
+    assert call(n=0) == -1
+    assert call(n=65) == -1
+    assert call(f0=3, n=13) == -1
+    assert call(k=A + 8) == -3
+    assert call(ts=A + 2) == -3
+    assert call(shots=None) == -1
+    assert call(c=_desc(format_tag=7)) == -4
+    assert call(c=_desc(sink_per_shot=1)) == -1
 
 
 def test_rope_validation_before_launch():
