@@ -2,9 +2,12 @@
 
 One step = the whole hot path for one chunk of one attention layer, in
 steady state (sink + full window):
-    fp4kv_rope_rel(Q) -> fp4kv_quantize_append(K, V) -> fp4kv_attention_chunk
-on seeded synthetic inputs already resident in device memory.  The stream
-keeps going (the ring wraps); inputs rotate over 8 pre-drawn chunks.
+    fp4kv_rope_append(Q, K, V) -> fp4kv_attention_chunk
+(the queries' rotation fused with the append's amax pass, then the encode,
+then attention) on seeded synthetic inputs already resident in device
+memory.  The stream keeps going (the ring wraps); inputs rotate over 16
+sets (8 seeded draws and their negations, 690 MB for the 1.3B-like layer,
+more than the 256 MB Infinity Cache holds).
 
 Workload (default): one layer shaped like the 1.3B generator: 12 heads,
 head_dim 128, 1560 tokens/frame, chunk 3 frames, sink 3 + window 12 frames,
@@ -14,15 +17,20 @@ Printed: one JSON line.  value = frames/s of one layer = C * K / time of K
 steps.  roofline = the attention kernel (the dominant one): algorithmic
 FLOP per launch (4*D per (query, key) pair the masks keep) / its mean
 duration from HIP events on the launch stream, against the 2.5 PFLOP/s
-dense f16/bf16 MFMA peak.  roofline_codec = the two append kernels:
-algorithmic bytes (kept K and V read once, codes and scales written once)
-/ their mean duration, against 8 TB/s.  cpu_baseline = the CPU oracle on a
-bounded sample of the same step.
+dense f16/bf16 MFMA peak.  roofline_codec = the step's codec kernels as
+timed inside the steps (rotation + append): algorithmic bytes (queries read
+and written as float32, kept K and V read once, codes and scales written
+once) / their mean duration, against 8 TB/s.  codec = the append alone and
+the fused call by the cold protocol (inputs rotating over the sets) and
+hot (one set), beside a plain copy of the same K and V bytes.  configs = the
+5B-like, multi-shot and long-stream layers at steady state.  cpu_baseline =
+the CPU oracle on a bounded sample of the same step.
 
 --kv nvfp4_rot stores keys rotated; the step becomes
-    fp4kv_quantize_append_rotated(K, V) -> fp4kv_rope_rel(Q) -> fp4kv_attention_chunk
-and roofline_codec covers the first (the cache update: the append plus the
-re-encoding of the window keys that survive the window move).
+    fp4kv_quantize_append_rotated(K, V) -> fp4kv_rope_rel_frames(Q) -> fp4kv_attention_chunk
+and roofline_codec covers the first two (the cache update with the
+re-encoding of the window keys that survive the window move, and the
+rotation).  --kv bf16 is the unquantized baseline cache.
 """
 from __future__ import annotations
 
@@ -56,6 +64,8 @@ def parse():
                     help="attention workgroups (0: the library's default, one per compute unit "
                          "with at least 4 key tiles each)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the codec protocol and the other configurations (profiling runs)")
     ap.add_argument("--traffic-json", default=None,
                     help="per-launch HBM bytes measured with rocprofv3 counters "
                          "(default: profiles/traffic_<workload>.json)")
@@ -211,6 +221,203 @@ def surviving_window_frames(w, f0, per_shot, shot_start):
                if not (per_shot and f - shot_start(f) < w.S))
 
 
+def draw_sets(w, n_base, dev):
+    """2 * n_base input sets (Q, K, V) of one chunk in device memory: n_base
+    seeded draws and their negations (same statistics, other bytes), so
+    that a set is cold in the 256 MB Infinity Cache when it comes round."""
+    import numpy as np
+    import torch
+
+    from fp4_kv_cache_fp4kv_amd import workloads as wl
+
+    def dev_t(vals, bits):
+        if bits is not None:
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(vals).to(dev)
+
+    n_tok = w.C * w.T
+    sets = [tuple(dev_t(*wl.draw(w, c, tid, n_tokens=n_tok)) for tid in (wl.Q_ID, wl.K_ID, wl.V_ID))
+            for c in range(n_base)]
+    return sets + [tuple(torch.neg(t) for t in s) for s in sets]
+
+
+def shot_start_fn(w):
+    def shot_start(f):
+        s0 = w.shot_of(f)
+        while f > 0 and w.shot_of(f - 1) == s0:
+            f -= 1
+        return f
+    return shot_start
+
+
+def measure(w, steps, warmup, sets, kv="nvfp4", sink_per_shot=False, workgroups=0):
+    """Steady-state steps of one layer: the cache update (with the queries'
+    rotation when it is fused) and attention, each bracketed by HIP events
+    on the launch stream; the whole K steps bracketed by synchronizations."""
+    import torch
+
+    from fp4_kv_cache_fp4kv_amd import api
+
+    dev = torch.device("cuda:0")
+    gc = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride, device="cuda:0",
+                        kv_format=kv, sink_per_shot=sink_per_shot)
+    shot_start = shot_start_fn(w)
+    qrot = torch.empty((w.C * w.T, w.H, w.D), dtype=torch.float32, device=dev)
+    out = torch.empty((w.C * w.T, w.H, w.D), dtype=torch.bfloat16, device=dev)
+    rot = kv == "nvfp4_rot"
+    fused = kv == "nvfp4"   # one rope_append call: rotation fused with the amax pass
+    first = -(-(w.S + w.W) // w.C)       # first chunk step with a full window
+    ev = {k: [] for k in ("a0", "a1", "c0", "c1")}
+
+    def step(c, record):
+        q, k, v = sets[c % len(sets)]
+        f0 = c * w.C
+        shots = [w.shot_of(f) for f in range(f0, f0 + w.C)]
+        fss = [shot_start(f) for f in range(f0, f0 + w.C)] if sink_per_shot else None
+        if record:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record()
+        if fused:   # the queries' rotation and the append: two kernels
+            api.rope_append(gc, q, k, v, f0, w.C, shots, shot_starts=fss, q_out=qrot)
+        elif rot:   # turn the surviving window keys, store the new keys rotated
+            api.quantize_append_rotated(gc, k, v, f0, w.C, shots, shot_starts=fss)
+        else:
+            api.quantize_append(gc, k, v, f0, w.C, shots, shot_starts=fss)
+        if not fused:
+            api.rope_rel_frames(gc, q, f0, w.C, shot_starts=fss, out=qrot)
+        if record:
+            e[1].record()
+            e[2].record()
+        api.attention_chunk(gc, qrot, f0, w.C, shots, out=out, n_workgroups=workgroups)
+        if record:
+            e[3].record()
+            ev["c0"].append(e[0]); ev["c1"].append(e[1])
+            ev["a0"].append(e[2]); ev["a1"].append(e[3])
+
+    for c in range(first):                # fill the sink and window
+        step(c, False)
+    c = first
+    for _ in range(warmup):
+        step(c, False)
+        c += 1
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step(c, True)
+        c += 1
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    attn_each = sorted(a.elapsed_time(b) for a, b in zip(ev["a0"], ev["a1"]))
+    update_ms = sum(a.elapsed_time(b) for a, b in zip(ev["c0"], ev["c1"])) / steps
+    f0s = [(c - steps + i) * w.C for i in range(steps)]
+    # useful FLOP: only the (query frame, key frame) pairs the masks keep,
+    # averaged over the timed steps (equal to 4 H Nq Nk D without shots)
+    pairs = [visible_pairs(w, f0, sink_per_shot, shot_start) for f0 in f0s]
+    flops = 4.0 * w.H * w.T * w.Tc * w.D * sum(pairs) / len(pairs)
+    attn_ms = sum(attn_each) / steps
+    es = 2 if w.dtype == "bf16" else 4
+    kept = 2 * w.C * w.Tc * w.H * w.D
+    update_bytes = kept * es + kept * (2.0 if kv == "bf16" else 0.5 + 1.0 / 16.0)
+    q_elems = w.C * w.T * w.H * w.D
+    update_bytes += q_elems * (es + 4)      # the queries: read, written as float32
+    if rot:
+        # the re-encoding of the surviving window keys (their codes and
+        # scales read and written once)
+        surv = [surviving_window_frames(w, f0, sink_per_shot, shot_start) for f0 in f0s]
+        key_frame = w.H * w.Tc * (w.D // 2 + w.D // 16)
+        update_bytes += 2.0 * key_frame * sum(surv) / len(surv)
+    del gc
+    return {"ms_step": ms_step, "attn_ms": attn_ms, "attn_each": attn_each,
+            "update_ms": update_ms, "update_bytes": update_bytes, "flops": flops,
+            "pairs": sum(pairs) / len(pairs)}
+
+
+def time_calls(fn, n_calls, reps=3):
+    """Mean microseconds per call of fn(i), i = 0 .. n_calls - 1, from HIP
+    events on the current stream around the whole loop (best of reps)."""
+    import torch
+    fn(0)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n_calls):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / n_calls * 1e3
+        best = us if best is None else min(best, us)
+    return best
+
+
+def codec_measure(w, sets):
+    """The codec at the per-step size by the cold-cache protocol: inputs
+    rotate over the sets (cold) or repeat one set (hot); beside them a plain
+    device copy of the appended K and V bytes (the practical ceiling), cold
+    over as many buffers as the sets and hot."""
+    import torch
+
+    from fp4_kv_cache_fp4kv_amd import api
+
+    gc = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride, device="cuda:0")
+    es = 2 if w.dtype == "bf16" else 4
+    kept = 2 * w.C * w.Tc * w.H * w.D
+    append_bytes = kept * es + kept * (0.5 + 1.0 / 16.0)
+    q_elems = w.C * w.T * w.H * w.D
+    prologue_bytes = append_bytes + q_elems * (es + 4)
+    qrot = torch.empty((w.C * w.T, w.H, w.D), dtype=torch.float32, device="cuda:0")
+    shots = [0] * w.C
+    n = len(sets)
+
+    def app(i, cold):
+        q, k, v = sets[i % n if cold else 0]
+        api.quantize_append(gc, k, v, 0, w.C, shots)
+
+    def pro(i, cold):
+        q, k, v = sets[i % n if cold else 0]
+        api.rope_append(gc, q, k, v, 0, w.C, shots, q_out=qrot)
+
+    res = {}
+    for name, fn, b in (("append", app, append_bytes), ("rope_append", pro, prologue_bytes)):
+        cold = time_calls(lambda i: fn(i, True), 4 * n)
+        hot = time_calls(lambda i: fn(i, False), 4 * n)
+        res[name] = {"bytes": int(b), "cold_us": round(cold, 2), "hot_us": round(hot, 2),
+                     "cold_GBs": round(b / cold / 1e3, 1), "hot_GBs": round(b / hot / 1e3, 1),
+                     "cold_frac": round(b / cold / 1e3 / HBM_PEAK_GBS, 4),
+                     "hot_frac": round(b / hot / 1e3 / HBM_PEAK_GBS, 4)}
+    # plain copy of the appended K and V (read and written once each)
+    nbytes = kept * es
+    srcs = [torch.empty(nbytes // 2, dtype=torch.int16, device="cuda:0").fill_(i) for i in range(n)]
+    dsts = [torch.empty_like(srcs[0]) for _ in range(n)]
+    cold = time_calls(lambda i: dsts[i % n].copy_(srcs[i % n]), 4 * n)
+    hot = time_calls(lambda i: dsts[0].copy_(srcs[0]), 4 * n)
+    res["copy"] = {"bytes": int(2 * nbytes), "cold_us": round(cold, 2), "hot_us": round(hot, 2),
+                   "cold_GBs": round(2 * nbytes / cold / 1e3, 1),
+                   "hot_GBs": round(2 * nbytes / hot / 1e3, 1)}
+    res["sets"] = n
+    res["set_MB"] = round(sum(t.numel() * t.element_size() for t in sets[0]) / 1e6, 1)
+    del gc, srcs, dsts
+    torch.cuda.empty_cache()
+    return res
+
+
+def summary(w, m):
+    tflops = m["flops"] / (m["attn_ms"] * 1e-3) / 1e12
+    return {"workload": workload_desc(w), "ms_per_step": round(m["ms_step"], 4),
+            "frames_per_s": round(w.C / (m["ms_step"] * 1e-3), 1),
+            "attention_ms": round(m["attn_ms"], 4),
+            "attention_only_frames_per_s": round(w.C / (m["attn_ms"] * 1e-3), 1),
+            "useful_TFLOPs": round(tflops, 1), "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+            "frame_pairs_per_step": round(m["pairs"], 2),
+            "update_ms": round(m["update_ms"], 4),
+            "update_frac": round(m["update_bytes"] / (m["update_ms"] * 1e-3) / 1e9
+                                 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -225,112 +432,17 @@ def main():
               "(the path shards by head or by time, see the design notes)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from fp4_kv_cache_fp4kv_amd import api
     from fp4_kv_cache_fp4kv_amd import workloads as wl
 
     w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    gc = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride, device="cuda:0",
-                        kv_format=args.kv, sink_per_shot=args.sink_per_shot)
-
-    def shot_start(f):
-        s0 = w.shot_of(f)
-        while f > 0 and w.shot_of(f - 1) == s0:
-            f -= 1
-        return f
-
-    def dev_t(vals, bits):
-        if bits is not None:
-            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(vals).to(dev)
-
-    n_sets = 8
-    sets = []
-    n_tok = w.C * w.T
-    for c in range(n_sets):
-        sets.append(tuple(dev_t(*wl.draw(w, c, tid, n_tokens=n_tok))
-                          for tid in (wl.Q_ID, wl.K_ID, wl.V_ID)))
-    qrot = torch.empty((w.C * w.T, w.H, w.D), dtype=torch.float32, device=dev)
-    rot = args.kv == "nvfp4_rot"
-    out = torch.empty((w.C * w.T, w.H, w.D), dtype=torch.bfloat16, device=dev)
-    first = -(-(w.S + w.W) // w.C)       # first chunk step with a full window
-
-    ev = {k: [] for k in ("a0", "a1", "c0", "c1")}
-
-    def step(c, record):
-        q, k, v = sets[c % n_sets]
-        f0 = c * w.C
-        shots = [w.shot_of(f) for f in range(f0, f0 + w.C)]
-        fss = [shot_start(f) for f in range(f0, f0 + w.C)] if args.sink_per_shot else None
-        def rope(x, y):
-            if fss is None:
-                api.rope_rel(x, api.cache_positions(w.S, w.W, f0, w.C), w.T, gc.cos_sin, out=y)
-            else:   # per-frame positions (a cut inside the chunk breaks the sequence)
-                for j in range(w.C):
-                    rows = slice(j * w.T, (j + 1) * w.T)
-                    api.rope_rel(x[rows], api.frame_position(w.S, w.W, f0 + j, f0 + w.C, fss[j]),
-                                 w.T, gc.cos_sin, out=y[rows])
-
-        if record:
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            e[0].record()
-        if rot:   # turn the surviving window keys, store the new keys rotated
-            api.quantize_append_rotated(gc, k, v, f0, w.C, shots, shot_starts=fss)
-        else:
-            api.quantize_append(gc, k, v, f0, w.C, shots, shot_starts=fss)
-        if record:
-            e[1].record()
-        rope(q, qrot)
-        if record:
-            e[2].record()
-        api.attention_chunk(gc, qrot, f0, w.C, shots, out=out, n_workgroups=args.workgroups)
-        if record:
-            e[3].record()
-            ev["c0"].append(e[0]); ev["c1"].append(e[1])
-            ev["a0"].append(e[2]); ev["a1"].append(e[3])
-
-    for c in range(first):                # fill the sink and window
-        step(c, False)
-    c = first
-    for _ in range(args.warmup):
-        step(c, False)
-        c += 1
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(args.steps):
-        step(c, True)
-        c += 1
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    attn_each = sorted(a.elapsed_time(b) for a, b in zip(ev["a0"], ev["a1"]))
-    attn_ms = sum(attn_each) / args.steps
-    codec_ms = sum(a.elapsed_time(b) for a, b in zip(ev["c0"], ev["c1"])) / args.steps
+    sets = draw_sets(w, 8, dev)
+    m = measure(w, args.steps, args.warmup, sets, args.kv, args.sink_per_shot, args.workgroups)
     pct = lambda v, q: v[min(len(v) - 1, int(q * len(v)))]
-
-    Nq, Nk = w.C * w.T, (w.S + w.W) * w.Tc
-    # useful FLOP: only the (query frame, key frame) pairs the masks keep,
-    # averaged over the timed steps (equal to 4 H Nq Nk D without shots)
-    pairs = [visible_pairs(w, (c - args.steps + i) * w.C, args.sink_per_shot, shot_start)
-             for i in range(args.steps)]
-    flops = 4.0 * w.H * w.T * w.Tc * w.D * sum(pairs) / len(pairs)
-    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
-    es = 2 if w.dtype == "bf16" else 4
-    kept = 2 * w.C * w.Tc * w.H * w.D
-    codec_bytes = kept * es + kept * (2.0 if args.kv == "bf16" else 0.5 + 1.0 / 16.0)
-    if rot:
-        # cache update: the append plus the re-encoding of the surviving
-        # window keys (their codes and scales read and written once)
-        surv = [surviving_window_frames(w, (c - args.steps + i) * w.C, args.sink_per_shot,
-                                        shot_start) for i in range(args.steps)]
-        key_frame = w.H * w.Tc * (w.D // 2 + w.D // 16)
-        codec_bytes += 2.0 * key_frame * sum(surv) / len(surv)
-    codec_gbs = codec_bytes / (codec_ms * 1e-3) / 1e9
+    attn_tflops = m["flops"] / (m["attn_ms"] * 1e-3) / 1e12
+    update_gbs = m["update_bytes"] / (m["update_ms"] * 1e-3) / 1e9
 
     # HBM bytes per attention launch from rocprofv3 counters, valid only for
     # the kernel source they were taken on
@@ -344,14 +456,16 @@ def main():
     except (OSError, ValueError):
         pass
 
+    rot = args.kv == "nvfp4_rot"
+    Nq, Nk = w.C * w.T, (w.S + w.W) * w.Tc
     res = {
         "metric": METRIC,
-        "value": round(w.C / (ms_step * 1e-3), 3),
+        "value": round(w.C / (m["ms_step"] * 1e-3), 3),
         "unit": "latent frames/s per layer",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(m["ms_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -360,19 +474,42 @@ def main():
         "config": {"workload": workload_desc(w), "kv_format": args.kv,
                    "sink": "per_shot" if args.sink_per_shot else "stream", "query_rows": Nq,
                    "workgroups": args.workgroups or "default",
-                   "keys": Nk,
-                   "frames_per_step": w.C, "attention_ms": round(attn_ms, 4),
-                   "attention_only_frames_per_s": round(w.C / (attn_ms * 1e-3), 1),
-                   "attention_ms_p10_p50_p90": [round(pct(attn_each, q), 4)
+                   "keys": Nk, "input_sets": len(sets),
+                   "frames_per_step": w.C, "attention_ms": round(m["attn_ms"], 4),
+                   "attention_only_frames_per_s": round(w.C / (m["attn_ms"] * 1e-3), 1),
+                   "attention_ms_p10_p50_p90": [round(pct(m["attn_each"], q), 4)
                                                 for q in (0.1, 0.5, 0.9)],
-                   ("cache_update_ms" if rot else "append_ms"): round(codec_ms, 4)},
+                   ("cache_update_ms" if rot else "rope_append_ms"): round(m["update_ms"], 4)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic},
-        "roofline_codec": {"bound": "hbm", "achieved": round(codec_gbs, 1), "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": round(codec_gbs / HBM_PEAK_GBS, 4),
-                           "bytes": int(codec_bytes)},
+        # the step's codec kernels as timed inside the steps: for the NVFP4
+        # path the queries' rotation fused with the append (rope_amax_kernel,
+        # encode_kernel); bytes = queries read and written as float32, kept
+        # K and V read once, codes and scales written once
+        "roofline_codec": {"bound": "hbm", "achieved": round(update_gbs, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(update_gbs / HBM_PEAK_GBS, 4),
+                           "bytes": int(m["update_bytes"]),
+                           "kernels": {"nvfp4": "rope_amax_kernel + encode_kernel",
+                                       "nvfp4_rot": "amax_kernel + encode_kernel + rope_kernel",
+                                       "bf16": "store_bf16_kernel + rope_kernel"}[args.kv]},
     }
+    if args.kv == "nvfp4" and not args.no_extra:
+        res["codec"] = codec_measure(w, sets)
+    del sets
+    torch.cuda.empty_cache()
+    if args.kv == "nvfp4" and not args.no_extra and args.workload == "l13b":
+        # the other full-size configurations, each at steady state
+        configs = {}
+        for name, per_shot in (("l5b", False), ("l5b_shots", False), ("long", False)):
+            wc = wl.WORKLOADS[name]
+            sc = draw_sets(wc, 4, dev)
+            mc = measure(wc, 20, 3, sc, "nvfp4", per_shot, args.workgroups)
+            configs[name] = summary(wc, mc)
+            configs[name]["codec"] = codec_measure(wc, sc)
+            del sc
+            torch.cuda.empty_cache()
+        res["configs"] = configs
     if not args.no_cpu_baseline and args.kv == "nvfp4":
         res["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(res), flush=True)

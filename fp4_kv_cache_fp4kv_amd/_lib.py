@@ -30,7 +30,8 @@ EXPORTED = ("fp4kv_strerror", "fp4kv_abi_version", "fp4kv_cache_nbytes", "fp4kv_
             "fp4kv_append_workspace_bytes", "fp4kv_quantize_append", "fp4kv_rope_table",
             "fp4kv_rope_rel", "fp4kv_attention_chunk", "fp4kv_attention_workspace_bytes",
             "fp4kv_rerotate_window", "fp4kv_quantize_append_rotated",
-            "fp4kv_quantize_append_noalloc")
+            "fp4kv_quantize_append_noalloc", "fp4kv_frame_position", "fp4kv_rope_rel_frames",
+            "fp4kv_rope_append")
 
 
 class CacheDesc(ctypes.Structure):
@@ -95,6 +96,15 @@ def load() -> ctypes.CDLL:
     lib.fp4kv_quantize_append_noalloc.argtypes = [P(CacheDesc), vp, vp, c_int, c_i32, c_i32,
                                                   P(c_i32), P(c_i32), vp, vp]
     lib.fp4kv_quantize_append_noalloc.restype = c_int
+    lib.fp4kv_frame_position.argtypes = [P(CacheDesc), c_i32, c_i32, c_i32]
+    lib.fp4kv_frame_position.restype = c_int
+    lib.fp4kv_rope_rel_frames.argtypes = [P(CacheDesc), vp, c_int, vp, c_int, c_i32, c_i32,
+                                          P(c_i32), vp, c_i32, vp]
+    lib.fp4kv_rope_rel_frames.restype = c_int
+    lib.fp4kv_rope_append.argtypes = [P(CacheDesc), vp, c_int, vp, c_int, vp, vp, c_int, c_i32,
+                                      c_i32, P(c_i32), P(c_i32), vp, c_i32, vp, ctypes.c_size_t,
+                                      vp]
+    lib.fp4kv_rope_append.restype = c_int
     lib.fp4kv_rerotate_window.argtypes = [P(CacheDesc), c_i32, c_i32, vp, c_i32, vp,
                                           ctypes.c_size_t, vp]
     lib.fp4kv_rerotate_window.restype = c_int

@@ -280,18 +280,68 @@ def attention_chunk(cache: FP4KVCache, q_rot: torch.Tensor, q_frame0: int, n_q_f
     return out
 
 
-def frame_position(S: int, W: int, f: int, f1: int, shot_start: Optional[int] = None) -> int:
-    """Cache-relative position of frame f at a step ending at frame f1: with
-    per-shot sinks (shot_start given) f - shot_start inside the shot's first
-    S frames, else S + f - max(S, f1 - W); without, f for f < S."""
-    ws = max(S, f1 - W)
-    rel = f if shot_start is None else f - shot_start
-    return rel if rel < S else S + (f - ws)
+def frame_position(cache: FP4KVCache, f: int, f1: int, shot_start: Optional[int] = None) -> int:
+    """fp4kv_frame_position: cache-relative position of frame f at the step
+    ending at frame f1 (shot_start: first frame of f's shot, per-shot sinks)."""
+    pos = load().fp4kv_frame_position(ctypes.byref(cache.desc), int(f), int(f1),
+                                      0 if shot_start is None else int(shot_start))
+    check(min(pos, 0), "fp4kv_frame_position")
+    return pos
 
 
-def cache_positions(S: int, W: int, f0: int, n: int) -> int:
-    """Cache-relative position of the first query frame of a step (its
-    pos0 for rope_rel): f0 if f0 < S, else S + f0 - max(S, f0 + n - W)."""
-    f1 = f0 + n
-    ws = max(S, f1 - W)
-    return f0 if f0 < S else S + (f0 - ws)
+def rope_rel_frames(cache: FP4KVCache, x: torch.Tensor, frame0: int, n_frames: int,
+                    shot_starts: Optional[Sequence[int]] = None,
+                    out: Optional[torch.Tensor] = None, out_dtype=torch.float32) -> torch.Tensor:
+    """fp4kv_rope_rel_frames: rotate one chunk's tensor x [n_frames*T][H][D]
+    by its frames' cache-relative positions (computed by the library) at the
+    window ending at frame0 + n_frames.  shot_starts (first frame of each
+    frame's shot) is required by a cache with per-shot sinks."""
+    _require(x, "x", None, cache.device)
+    if x.dtype not in _DTYPES or x.shape != (n_frames * cache.T, cache.H, cache.D):
+        raise ValueError(f"x must be float32/bfloat16 {(n_frames * cache.T, cache.H, cache.D)}")
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    _require(out, "out", None, x.device)
+    if out.dtype not in _DTYPES or out.shape != x.shape:
+        raise ValueError("out must be float32/bfloat16 with the shape of x")
+    st = load().fp4kv_rope_rel_frames(
+        ctypes.byref(cache.desc), x.data_ptr(), _DTYPES[x.dtype], out.data_ptr(),
+        _DTYPES[out.dtype], frame0, n_frames,
+        None if shot_starts is None else _i32_array(shot_starts), cache.cos_sin.data_ptr(),
+        cache.n_pos, _stream(cache.device))
+    check(st, "fp4kv_rope_rel_frames")
+    return out
+
+
+def rope_append(cache: FP4KVCache, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                frame0: int, n_frames: int, shots: Sequence[int],
+                shot_starts: Optional[Sequence[int]] = None,
+                q_out: Optional[torch.Tensor] = None, q_out_dtype=torch.float32) -> torch.Tensor:
+    """fp4kv_rope_append on the current stream: rotate the chunk's queries
+    (as rope_rel_frames) and append its keys and values (as quantize_append
+    with computed tensor scales) in two kernels.  Returns the rotated
+    queries."""
+    if cache.kv_format != "nvfp4":
+        raise ValueError("rope_append needs a cache with kv_format 'nvfp4'")
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, nm, device=cache.device)
+    shape = (n_frames * cache.T, cache.H, cache.D)
+    if k.dtype != v.dtype or k.dtype not in _DTYPES or q.dtype not in _DTYPES:
+        raise ValueError("q, k and v must be float32 or bfloat16 (k and v alike)")
+    if q.shape != shape or k.shape != shape or v.shape != shape:
+        raise ValueError(f"q/k/v must have shape {shape}")
+    if len(shots) != n_frames:
+        raise ValueError("one shot id per frame")
+    if q_out is None:
+        q_out = torch.empty(shape, dtype=q_out_dtype, device=q.device)
+    _require(q_out, "q_out", None, cache.device)
+    if q_out.dtype not in _DTYPES or q_out.shape != shape:
+        raise ValueError("q_out must be float32/bfloat16 with the shape of q")
+    st = load().fp4kv_rope_append(
+        ctypes.byref(cache.desc), q.data_ptr(), _DTYPES[q.dtype], q_out.data_ptr(),
+        _DTYPES[q_out.dtype], k.data_ptr(), v.data_ptr(), _DTYPES[k.dtype], frame0, n_frames,
+        _i32_array(shots), None if shot_starts is None else _i32_array(shot_starts),
+        cache.cos_sin.data_ptr(), cache.n_pos, cache.workspace.data_ptr(),
+        cache.workspace.numel(), _stream(cache.device))
+    check(st, "fp4kv_rope_append")
+    return q_out

@@ -14,7 +14,7 @@ using namespace fp4kv;
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -179,6 +179,63 @@ int prepare_window_move(AppendParams &p, const fp4kv_cache *c, int32_t f1_from, 
   return FP4KV_OK;
 }
 
+// Cache-relative position of frame f at the step whose frames end at f1:
+// a sink frame keeps its index from the sink's anchor (frame 0, or with
+// per-shot sinks its shot's first frame fs); a window frame is S + (f - ws)
+// with ws = max(S, f1 - W).  -1 for a frame that is neither.
+long long frame_pos(const fp4kv_cache *c, long long f, long long f1, long long fs) {
+  const long long S = c->sink_frames;
+  const long long rel = c->sink_per_shot ? f - fs : f;
+  if (f < 0 || f >= f1 || rel < 0) return -1;
+  if (rel < S) return rel;
+  const long long ws = std::max<long long>(S, f1 - c->window_frames);
+  return f < ws ? -1 : S + (f - ws);
+}
+
+// Rotation of the chunk frame0 .. frame0 + n_frames - 1 of a tensor
+// [n_frames * T][H][D] by the frames' cache-relative positions at the window
+// ending at f1 = frame0 + n_frames, positions computed here per frame.
+int prepare_rope_frames(RopeParams &p, const fp4kv_cache *c, const void *x, int in_dtype, void *y,
+                        int out_dtype, int32_t frame0, int32_t n_frames,
+                        const int32_t *frame_shot_start, const float *cos_sin, int32_t n_pos) {
+  if (!x || !y) return FP4KV_EINVAL;
+  if (in_dtype != FP4KV_F32 && in_dtype != FP4KV_BF16) return FP4KV_EINVAL;
+  if (out_dtype != FP4KV_F32 && out_dtype != FP4KV_BF16) return FP4KV_EINVAL;
+  if (frame0 < 0 || n_frames < 1 || n_frames > FP4KV_MAX_FRAMES) return FP4KV_EINVAL;
+  if ((long long)frame0 + n_frames > (1ll << 30)) return FP4KV_EINVAL;
+  if (c->sink_per_shot && !frame_shot_start) return FP4KV_EINVAL;
+  if (c->rot_dim > 0 && (!cos_sin || n_pos < 1)) return FP4KV_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)cos_sin & 7u)) return FP4KV_EALIGN;
+  if (x == y && in_dtype != out_dtype) return FP4KV_EINVAL;
+  memset(&p, 0, sizeof(p));
+  const long long f1 = (long long)frame0 + n_frames;
+  for (int j = 0; j < n_frames; ++j) {
+    const long long f = (long long)frame0 + j;
+    long long fs = 0;
+    if (c->sink_per_shot) {
+      fs = frame_shot_start[j];
+      if (fs < 0 || fs > f) return FP4KV_EINVAL;
+    }
+    const long long pos = frame_pos(c, f, f1, fs);
+    if (pos < 0) return FP4KV_EINVAL;            // a frame outside sink and window
+    if (c->rot_dim > 0 && pos >= n_pos) return FP4KV_ESHAPE;
+    p.pos[j] = (int32_t)pos;
+  }
+  p.x = x;
+  p.y = y;
+  p.out_f32 = out_dtype == FP4KV_F32;
+  p.cos_sin = cos_sin;
+  p.n_tokens = (long long)n_frames * c->tokens_per_frame;
+  p.H = c->n_heads;
+  p.D = c->head_dim;
+  p.T = c->tokens_per_frame;
+  p.rot_dim = c->rot_dim;
+  p.in_bf16 = in_dtype == FP4KV_BF16;
+  p.per_frame = 1;
+  if (p.n_tokens * p.H * (long long)p.D > (1ll << 40)) return FP4KV_ESHAPE;
+  return FP4KV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -338,6 +395,7 @@ int fp4kv_rope_rel(const void *x, int in_dtype, void *y, int out_dtype, int64_t 
   if (n_tokens > (1ll << 40) || n_tokens * n_heads * (long long)head_dim > (1ll << 40))
     return FP4KV_ESHAPE;
   RopeParams p;
+  memset(&p, 0, sizeof(p));
   p.x = x;
   p.y = y;
   p.out_f32 = out_dtype == FP4KV_F32;
@@ -350,6 +408,48 @@ int fp4kv_rope_rel(const void *x, int in_dtype, void *y, int out_dtype, int64_t 
   p.rot_dim = rot_dim;
   p.in_bf16 = in_dtype == FP4KV_BF16;
   return from_hip(launch_rope(p, (hipStream_t)stream));
+}
+
+int fp4kv_frame_position(const fp4kv_cache *c, int32_t frame, int32_t f1, int32_t shot_start) {
+  int st = check_shape(c);
+  if (st) return st;
+  if (frame < 0 || f1 > (1 << 30) || (c->sink_per_shot && (shot_start < 0 || shot_start > frame)))
+    return FP4KV_EINVAL;
+  const long long pos = frame_pos(c, frame, f1, c->sink_per_shot ? shot_start : 0);
+  return pos < 0 ? FP4KV_EINVAL : (int)pos;
+}
+
+int fp4kv_rope_rel_frames(const fp4kv_cache *c, const void *x, int in_dtype, void *y,
+                          int out_dtype, int32_t frame0, int32_t n_frames,
+                          const int32_t *frame_shot_start, const float *cos_sin, int32_t n_pos,
+                          void *stream) {
+  int st = check_shape(c);
+  if (st) return st;
+  RopeParams p;
+  if ((st = prepare_rope_frames(p, c, x, in_dtype, y, out_dtype, frame0, n_frames,
+                                frame_shot_start, cos_sin, n_pos)))
+    return st;
+  return from_hip(launch_rope(p, (hipStream_t)stream));
+}
+
+int fp4kv_rope_append(const fp4kv_cache *c, const void *q, int q_dtype, void *q_rot,
+                      int q_rot_dtype, const void *k, const void *v, int kv_dtype, int32_t frame0,
+                      int32_t n_frames, const int32_t *frame_shot, const int32_t *frame_shot_start,
+                      const float *cos_sin, int32_t n_pos, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  AppendParams ap;
+  int st = prepare_append(ap, c, k, v, kv_dtype, frame0, n_frames, frame_shot, frame_shot_start,
+                          nullptr);
+  if (st) return st;
+  if (c->format_tag != FP4KV_FORMAT_NVFP4_V1) return FP4KV_EINVAL;
+  if ((st = check_append_ws(workspace, workspace_bytes))) return st;
+  set_append_ws(ap, workspace);
+  RopeParams rp;
+  if ((st = prepare_rope_frames(rp, c, q, q_dtype, q_rot, q_rot_dtype, frame0, n_frames,
+                                frame_shot_start, cos_sin, n_pos)))
+    return st;
+  if (q_rot == k || q_rot == v) return FP4KV_EINVAL;   // K and V are read by both kernels
+  return from_hip(launch_rope_append(rp, ap, (hipStream_t)stream));
 }
 
 int fp4kv_attention_chunk(const fp4kv_cache *c, const void *q_rot, int q_dtype, void *o,
@@ -402,6 +502,7 @@ int fp4kv_attention_chunk(const fp4kv_cache *c, const void *q_rot, int q_dtype, 
   p.Nq = (int)nq;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   p.sink_per_shot = c->sink_per_shot;
+  p.sat_half = c->rot_dim / 2;
   for (int j = 0; j < n_q_frames; ++j) p.q_shot[j] = q_shot[j];
 
   // Work split: equal ranges of the virtual key tiles (n_v per row block)

@@ -257,9 +257,15 @@ __device__ __forceinline__ void load_v(const SlotRes &sr, int Tv, int k0, int lt
   }
 }
 
-// Two bf16 values (a 32-bit word) -> f16x2 bits; exact within the f16 range.
+// Largest finite f16: the MFMA operands are f16.
+constexpr float kF16Max = 65504.0f;
+
+// Two bf16 values (a 32-bit word) -> f16x2 bits; exact within the f16 range,
+// values beyond it saturate to +-65504.
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
-  const f16x2 h = {(_Float16)__uint_as_float(w << 16), (_Float16)__uint_as_float(w & 0xFFFF0000u)};
+  const float a = __builtin_amdgcn_fmed3f(__uint_as_float(w << 16), -kF16Max, kF16Max);
+  const float b = __builtin_amdgcn_fmed3f(__uint_as_float(w & 0xFFFF0000u), -kF16Max, kF16Max);
+  const f16x2 h = {(_Float16)a, (_Float16)b};
   return bits(h);
 }
 
@@ -714,6 +720,27 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = row_ok ? x[e] : 0.0f;
+            // The f16 range bounds the query operands: a rotary pair whose
+            // norm exceeds 65504 is scaled to norm 65504 (turns keep a
+            // pair's norm, so no later turn leaves the range), an element
+            // past the rotary pairs is clamped to +-65504.
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (8 * kk + 4 * hf + e < p.sat_half) {
+                // norm taken on values scaled by 2^-66 so that no finite
+                // input overflows the square
+                const float sa = x[2 * e] * 0x1p-66f, sb = x[2 * e + 1] * 0x1p-66f;
+                const float n2 = sa * sa + sb * sb;
+                if (n2 > (kF16Max * 0x1p-66f) * (kF16Max * 0x1p-66f)) {
+                  const float f = (kF16Max * 0x1p-66f) * __builtin_amdgcn_rsqf(n2);
+                  x[2 * e] *= f;
+                  x[2 * e + 1] *= f;
+                }
+              } else {
+                x[2 * e] = __builtin_amdgcn_fmed3f(x[2 * e], -kF16Max, kF16Max);
+                x[2 * e + 1] = __builtin_amdgcn_fmed3f(x[2 * e + 1], -kF16Max, kF16Max);
+              }
+            }
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = (float)qhi[kk][e] + (float)qlo[kk][e];

@@ -15,6 +15,7 @@
 
 #include "fp4kv_device.hpp"
 #include "internal.hpp"
+#include "rope_unit.hpp"
 
 namespace fp4kv {
 namespace {
@@ -71,6 +72,38 @@ __device__ __forceinline__ void load_key_block(const AppendParams &p, int j, int
 // workgroup's share of the slot's (key row, block) pairs.
 __device__ __forceinline__ void rerot_amax(const AppendParams &p, int s, uint32_t *red);
 
+// Partial max |x| of appended tensor y (0 = K, 1 = V) over the kept tokens,
+// taken by workgroup bx of nbx and stored as ws_partial[y][bx].
+__device__ __forceinline__ void amax_part(const AppendParams &p, int y, int bx, int nbx,
+                                          uint32_t *red) {
+  const bool bf16 = p.in_bf16;
+  const uint32_t row_chunks = (uint32_t)(p.H * p.D * (bf16 ? 2 : 4) / 16);  // one token
+  const uint32_t n_chunks = (uint32_t)(p.n_frames * p.Tc) * row_chunks;
+  const uint4 *base = (const uint4 *)p.x[y];
+  const uint32_t step = (uint32_t)nbx * kThreads;
+  uint32_t m = 0;
+  for (uint32_t c0 = (uint32_t)bx * kThreads + threadIdx.x; c0 < n_chunks;
+       c0 += step * kAmaxUnroll) {
+    uint4 v[kAmaxUnroll];
+#pragma unroll
+    for (int k = 0; k < kAmaxUnroll; ++k) {
+      const uint32_t c = c0 + k * step;
+      uint32_t addr = c;
+      if (p.stride != 1) {   // kept token r is stored token r * stride (frames hold T tokens)
+        const uint32_t r = c / row_chunks;
+        const uint32_t frame = r / (uint32_t)p.Tc, tc = r - frame * (uint32_t)p.Tc;
+        addr = (frame * (uint32_t)p.T + tc * (uint32_t)p.stride) * row_chunks + (c - r * row_chunks);
+      }
+      v[k] = c < n_chunks ? base[addr] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kAmaxUnroll; ++k) m = fold_max(m, v[k], bf16);
+  }
+  if (bf16) m = max(m & 0xFFFFu, m >> 16) << 16;   // bf16 bits -> float32 bits
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) p.ws_partial[y * kAmaxBlocks + bx] = m;
+}
+
 __global__ __launch_bounds__(kThreads) void amax_kernel(AppendParams p) {
   __shared__ uint32_t red[kThreads / 64];
   const int y = blockIdx.y;
@@ -99,32 +132,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(AppendParams p) {
     if (threadIdx.x == 0) p.ws_partial[blockIdx.x] = m;
     return;
   }
-  const bool bf16 = p.in_bf16;
-  const uint32_t row_chunks = (uint32_t)(p.H * p.D * (bf16 ? 2 : 4) / 16);  // one token
-  const uint32_t n_chunks = (uint32_t)(p.n_frames * p.Tc) * row_chunks;
-  const uint4 *base = (const uint4 *)p.x[y];
-  const uint32_t step = gridDim.x * kThreads;
-  uint32_t m = 0;
-  for (uint32_t c0 = blockIdx.x * kThreads + threadIdx.x; c0 < n_chunks;
-       c0 += step * kAmaxUnroll) {
-    uint4 v[kAmaxUnroll];
-#pragma unroll
-    for (int k = 0; k < kAmaxUnroll; ++k) {
-      const uint32_t c = c0 + k * step;
-      uint32_t addr = c;
-      if (p.stride != 1) {   // kept token r is stored token r * stride (frames hold T tokens)
-        const uint32_t r = c / row_chunks;
-        const uint32_t frame = r / (uint32_t)p.Tc, tc = r - frame * (uint32_t)p.Tc;
-        addr = (frame * (uint32_t)p.T + tc * (uint32_t)p.stride) * row_chunks + (c - r * row_chunks);
-      }
-      v[k] = c < n_chunks ? base[addr] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int k = 0; k < kAmaxUnroll; ++k) m = fold_max(m, v[k], bf16);
-  }
-  if (bf16) m = max(m & 0xFFFFu, m >> 16) << 16;   // bf16 bits -> float32 bits
-  m = block_max_u32(m, red);
-  if (threadIdx.x == 0) p.ws_partial[y * kAmaxBlocks + blockIdx.x] = m;
+  amax_part(p, y, (int)blockIdx.x, (int)gridDim.x, red);
 }
 
 // Tensor scale g = amax / 2688 from the kAmaxBlocks partial maxima of tensor
@@ -138,6 +146,13 @@ __device__ __forceinline__ float tensor_scale(const AppendParams &p, int y, uint
   m = block_max_u32(m, red);
   const float amax = __uint_as_float(m);
   return amax > 0.0f ? __fdiv_rn(amax, 2688.0f) : 1.0f;
+}
+
+// A caller-supplied tensor scale is used when it is finite and positive; any
+// other value (zero, negative, infinite, NaN) is replaced by 1, so the cache
+// never holds a scale that makes decoding or attention undefined.
+__device__ __forceinline__ float caller_scale(float g) {
+  return (g > 0.0f && g <= 3.4028235e38f) ? g : 1.0f;
 }
 
 // Encode one 16-element block: returns the two packed code words; *scale8
@@ -315,6 +330,24 @@ __device__ __forceinline__ void rerot_encode(const AppendParams &p, int rb, uint
   p.scales[0][row * nb + b] = (uint8_t)s8;
 }
 
+// The step's first kernel when queries are rotated and a chunk appended in
+// one call: workgroups [0, 2 kAmaxBlocks) take the partial maxima of K and V
+// (as amax_kernel), the rest rotate the queries (as rope_kernel).  The
+// encode kernel follows on the same stream.
+__global__ __launch_bounds__(kThreads) void rope_amax_kernel(RopeParams rp, AppendParams ap) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int b = (int)blockIdx.x;
+  if (b < 2 * kAmaxBlocks) {
+    amax_part(ap, b / kAmaxBlocks, b % kAmaxBlocks, kAmaxBlocks, red);
+    return;
+  }
+  const long long n = rope_units(rp);
+  const long long nb = (long long)gridDim.x - 2 * kAmaxBlocks;
+  for (long long u = (long long)(b - 2 * kAmaxBlocks) * kThreads + threadIdx.x; u < n;
+       u += nb * kThreads)
+    rope_unit(rp, u);
+}
+
 // One launch encodes both tensors.  Workgroups [0, p.v_blocks) encode the
 // values, dimension-major: one thread per (8 tokens, 16-block) writes one
 // 4-byte word (8 token nibbles) in each of the block's 16 dimension rows plus
@@ -332,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(AppendParams p) {
   }
   const bool is_v = (int)blockIdx.x < p.v_blocks;
   const int y = is_v ? 1 : 0;
-  const float g = p.tscale_in ? p.tscale_in[y] : tensor_scale(p, y, red);
+  const float g = p.tscale_in ? caller_scale(p.tscale_in[y]) : tensor_scale(p, y, red);
   const float d = 6.0f * g;
 
   if ((blockIdx.x == 0 || (int)blockIdx.x == p.v_blocks) && threadIdx.x < p.n_frames) {
@@ -543,16 +576,14 @@ hipError_t launch_cache_reset(const fp4kv_cache &c, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_append(const AppendParams &p_in, hipStream_t s) {
-  AppendParams p = p_in;
+namespace {
+
+// Workgroup counts of the encode kernel (and of the bf16 store kernel).
+void append_blocks(AppendParams &p) {
   if (p.bf16_cache) {
-    const long long k_units = (long long)p.n_frames * p.Tc * p.H * (p.D >> 3);
     const long long v_units = (long long)p.H * p.n_frames * (p.D >> 3) * (p.Tv >> 3);
     p.v_blocks = (int)((v_units + kThreads - 1) / kThreads);
-    const long long k_blocks = (k_units + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(store_bf16_kernel, dim3((unsigned)(p.v_blocks + k_blocks)), dim3(kThreads),
-                       0, s, p);
-    return hipGetLastError();
+    return;
   }
   const long long k_units = (long long)p.H * p.n_frames * p.Tc * (p.D >> 4);
   const long long v_units = (long long)p.H * p.n_frames * (p.Tv >> 3) * (p.D >> 4);
@@ -560,6 +591,27 @@ hipError_t launch_append(const AppendParams &p_in, hipStream_t s) {
   p.v_blocks = (int)((v_units + kThreads - 1) / kThreads);
   p.k_blocks = (int)((k_units + kThreads - 1) / kThreads);
   p.rr_blocks = p.rr_slots > 0 ? (int)((rr_units + kThreads - 1) / kThreads) : 0;
+}
+
+hipError_t launch_encode(const AppendParams &p, hipStream_t s) {
+  const long long blocks = (long long)p.v_blocks + p.k_blocks + (long long)p.rr_slots * p.rr_blocks;
+  if (blocks > 0)
+    hipLaunchKernelGGL(encode_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams &p_in, hipStream_t s) {
+  AppendParams p = p_in;
+  append_blocks(p);
+  if (p.bf16_cache) {
+    const long long k_units = (long long)p.n_frames * p.Tc * p.H * (p.D >> 3);
+    const long long k_blocks = (k_units + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(store_bf16_kernel, dim3((unsigned)(p.v_blocks + k_blocks)), dim3(kThreads),
+                       0, s, p);
+    return hipGetLastError();
+  }
   p.amax_tensors = (p.n_frames > 0 && !p.tscale_in) ? 2 : 0;
   const int amax_y = p.amax_tensors + p.rr_slots;
   if (amax_y > 0) {
@@ -567,10 +619,22 @@ hipError_t launch_append(const AppendParams &p_in, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const long long blocks = (long long)p.v_blocks + p.k_blocks + (long long)p.rr_slots * p.rr_blocks;
-  if (blocks > 0)
-    hipLaunchKernelGGL(encode_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+  return launch_encode(p, s);
+}
+
+hipError_t launch_rope_append(const RopeParams &rp, const AppendParams &ap_in, hipStream_t s) {
+  AppendParams ap = ap_in;   // NVFP4 cache, computed tensor scales, no window move
+  append_blocks(ap);
+  ap.amax_tensors = 2;
+  const long long n = rope_units(rp);
+  long long rope_blocks = (n + kThreads - 1) / kThreads;
+  if (rope_blocks > 8192) rope_blocks = 8192;
+  if (rope_blocks < 1) rope_blocks = 1;
+  hipLaunchKernelGGL(rope_amax_kernel, dim3((unsigned)(2 * kAmaxBlocks + rope_blocks)),
+                     dim3(kThreads), 0, s, rp, ap);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_encode(ap, s);
 }
 
 }  // namespace fp4kv

@@ -55,6 +55,8 @@ struct RopeParams {
   const float *cos_sin;
   long long n_tokens;
   int H, D, T, pos0, rot_dim, in_bf16, out_f32;
+  int per_frame;                    // 1: token t turns by pos[t / T], else pos0 + t / T
+  int32_t pos[FP4KV_MAX_FRAMES];
 };
 
 struct AttnParams {
@@ -68,6 +70,7 @@ struct AttnParams {
   int q_frame0, n_q_frames, Nq, q_f32;
   int bf16_cache;          // keys and values are bf16 (FP4KV_FORMAT_BF16_V1)
   int sink_per_shot;       // sink slots hold the first S frames of each shot
+  int sat_half;            // rotary pairs of the query (rot_dim / 2 of the cache)
   float scale_log2;        // softmax_scale * log2(e)
   int n_wg;                // workgroups of the split schedule
   float *ws_o;             // partial g_v * acc [2 n_wg][256 rows][D]
@@ -83,6 +86,9 @@ hipError_t launch_append(const AppendParams &p, hipStream_t s);
 // current device (resolved once per device).
 hipError_t append_scratch(void **out, size_t *bytes);
 hipError_t launch_rope(const RopeParams &p, hipStream_t s);
+// The queries' rotation and the append of one chunk in two kernels: the
+// rotation fused with the append's amax pass, then the encode.
+hipError_t launch_rope_append(const RopeParams &rp, const AppendParams &ap, hipStream_t s);
 hipError_t launch_attention(const AttnParams &p, int head_dim, int out_f32, hipStream_t s);
 
 // Attention workspace: FP4KV_MAX_WORKGROUPS counters, then per workgroup two

@@ -334,6 +334,59 @@ int fp4kv_rope_rel(const void *x, int in_dtype, void *y, int out_dtype, int64_t 
                    int32_t n_pos, void *stream);
 
 /*
+ * fp4kv_frame_position - cache-relative position of frame `frame` at the
+ * step whose frames end at f1 (KV-cache relative RoPE: refft.com, question
+ * "How do KV-cache relative RoPE and TriAttention work together ..."),
+ * host only.  With ws = max(S, f1 - W): a sink frame keeps its index from the
+ * sink's anchor (frame 0; with sink_per_shot = 1, shot_start, the first frame
+ * of its shot: position frame - shot_start when that is below S); a window
+ * frame ws <= frame < f1 is at S + (frame - ws).  shot_start is read only
+ * when sink_per_shot = 1.  Returns the position (>= 0), or FP4KV_EINVAL for
+ * a frame that is neither (or outside [0, f1)); descriptor errors as in
+ * fp4kv_cache_nbytes.  Pointer fields of `c` are not read.
+ */
+int fp4kv_frame_position(const fp4kv_cache *c, int32_t frame, int32_t f1, int32_t shot_start);
+
+/*
+ * fp4kv_rope_rel_frames - fp4kv_rope_rel of one chunk's tensor
+ * [n_frames * T][H][D] (T, H, D and rot_dim from the cache descriptor) with
+ * the positions computed by the library: token t of frame frame0 + j turns by
+ * fp4kv_frame_position(c, frame0 + j, frame0 + n_frames, frame_shot_start[j]),
+ * so frames need not have consecutive positions (per-shot sinks).  Same
+ * arithmetic, dtypes, alignment and aliasing rules as fp4kv_rope_rel.
+ *   frame_shot_start  host [n_frames], required when sink_per_shot = 1,
+ *               else may be NULL.
+ *   cos_sin     device table (fp4kv_rope_table, cache->rot_dim) with n_pos
+ *               rows, more than any position; NULL allowed when rot_dim = 0.
+ * Errors: FP4KV_EINVAL when a frame is neither a sink frame nor in the
+ * window ending at frame0 + n_frames; FP4KV_ESHAPE when a position is past
+ * the table.
+ */
+int fp4kv_rope_rel_frames(const fp4kv_cache *c, const void *x, int in_dtype, void *y,
+                          int out_dtype, int32_t frame0, int32_t n_frames,
+                          const int32_t *frame_shot_start, const float *cos_sin, int32_t n_pos,
+                          void *stream);
+
+/*
+ * fp4kv_rope_append - the two codec steps of one chunk in one call and two
+ * kernels: the rotation of the chunk's queries (fp4kv_rope_rel_frames of q
+ * into q_rot) and the append of its keys and values
+ * (fp4kv_quantize_append with tscale_in = NULL).  The first kernel rotates
+ * the queries and takes the partial maxima of K and V, the second encodes K
+ * and V into the cache ("fused RoPE" and "in-place quantized KV-cache
+ * updates", hysenlabs.com, section "NVFP4, sequence parallel and the async
+ * decode path").  Results are bit for bit those of the two separate calls.
+ * Arguments as in those calls; the cache must have format
+ * FP4KV_FORMAT_NVFP4_V1 (FP4KV_EINVAL otherwise).  q_rot must not be k or v
+ * (q_rot may be q when the dtypes match).
+ */
+int fp4kv_rope_append(const fp4kv_cache *c, const void *q, int q_dtype, void *q_rot,
+                      int q_rot_dtype, const void *k, const void *v, int kv_dtype, int32_t frame0,
+                      int32_t n_frames, const int32_t *frame_shot, const int32_t *frame_shot_start,
+                      const float *cos_sin, int32_t n_pos, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
  * fp4kv_attention_chunk - attention of the query frames
  * q_frame0 .. q_frame0+n_q_frames-1 over the NVFP4 cache, with FP4
  * dequantization fused into the attention loop.

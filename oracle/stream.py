@@ -97,7 +97,7 @@ class OracleCache:
         gs = []
         for idx, (x, tsc) in enumerate(((k, self.k_tscale), (v, self.v_tscale))):
             xk = self.kept(x, n_frames)                        # [n][Tc][H][D]
-            g = nvfp4.tensor_scale(xk) if tscale is None else np.float32(tscale[idx])
+            g = nvfp4.tensor_scale(xk) if tscale is None else self.caller_scale(tscale[idx])
             c, s8 = nvfp4.encode_blocks(xk, g)                 # codes per element
             for j in range(n_frames):
                 slot = self.slot(frame0 + j, fss[j])
@@ -120,6 +120,15 @@ class OracleCache:
             self.slot_shot[slot] = shots[j]
         return tuple(gs)
 
+    @staticmethod
+    def caller_scale(g):
+        """Reading (the pages fix none): a caller-supplied tensor scale is used
+        when it is finite and positive; zero, negative, infinite or NaN
+        scales are replaced by 1, so no cached scale makes decoding
+        undefined."""
+        g = np.float32(g)
+        return g if (np.isfinite(g) and g > 0) else np.float32(1.0)
+
     def decode_slot(self, slot):
         """(k_hat, v_hat) float32 [H][Tc][D] of one slot."""
         kh = nvfp4.decode_blocks(nvfp4.unpack_nibbles(self.k_codes[:, slot]),
@@ -130,6 +139,11 @@ class OracleCache:
                                  self.v_tscale[slot])
         return kh, vh
 
+    def operands(self, kh, vh):
+        """Decoded keys and values as attention uses them (NVFP4 values are
+        at most 6 * 448 * g in magnitude, so nothing changes here)."""
+        return kh, vh
+
     # ------------------------------------------------------------ positions
     def positions(self, frames, f1, shot_starts=None):
         if self.sink_per_shot:
@@ -137,13 +151,29 @@ class OracleCache:
                              for f, fs in zip(frames, shot_starts)])
         return np.array([ring.rel_pos(f, f1, self.S, self.W) for f in frames])
 
+    # Largest finite f16.  Reading (the pages fix no operand format): the
+    # attention operands are f16, so a query whose rotary pair (2i, 2i+1),
+    # i < rot_dim/2, has a norm above F16_MAX is scaled to norm F16_MAX (a
+    # turn keeps the norm, so the scaling commutes with the rotation), and a
+    # query element past rot_dim is clamped to +-F16_MAX.  Inputs within the
+    # f16 range are unchanged.
+    F16_MAX = 65504.0
+
     def rope_queries(self, q, q_frame0, n_q_frames, q_shot_starts=None):
         """Rotate q[n_q_frames*T][H][D] by the cache-relative positions of its
-        frames; float64 result."""
+        frames, then saturate it to the f16 range (F16_MAX); float64 result."""
         f1 = q_frame0 + n_q_frames
         pos = self.positions(range(q_frame0, f1), f1, q_shot_starts)
         pos_tok = np.repeat(pos, self.T)[:, None]           # [Nq, 1] over heads
-        return rope.rotate(q, pos_tok, self.rot_dim, self.base)
+        y = rope.rotate(q, pos_tok, self.rot_dim, self.base)
+        rd = self.rot_dim
+        a, b = y[..., 0:rd:2], y[..., 1:rd:2]
+        norm = np.sqrt(a * a + b * b)
+        f = np.where(norm > self.F16_MAX, self.F16_MAX / np.maximum(norm, 1.0), 1.0)
+        y[..., 0:rd:2] = a * f
+        y[..., 1:rd:2] = b * f
+        y[..., rd:] = np.clip(y[..., rd:], -self.F16_MAX, self.F16_MAX)
+        return y
 
     # ------------------------------------------------------------ attention
     def rotate_keys(self, k, kpos):
@@ -179,7 +209,7 @@ class OracleCache:
         slots = self.visible_slots(f1)
         keys, vals, kpos = [], [], []
         for slot, kf in slots:
-            kh, vh = self.decode_slot(slot)                    # [H][Tc][D]
+            kh, vh = self.operands(*self.decode_slot(slot))    # [H][Tc][D]
             keys.append(kh)
             vals.append(vh)
             if self.sink_per_shot:
@@ -260,6 +290,14 @@ class OracleCacheBF16(OracleCache):
     def decode_slot(self, slot):
         return (self.k_vals[:, slot].copy(),
                 self.v_vals[:, slot, :, :self.Tc].transpose(0, 2, 1).copy())
+
+    def operands(self, kh, vh):
+        """Reading (the pages fix no operand format): attention takes f16
+        operands, so stored bf16 keys and values beyond the f16 range
+        saturate to +-F16_MAX when attention reads them; the stored bf16
+        values themselves are unchanged."""
+        return (np.clip(kh, -self.F16_MAX, self.F16_MAX),
+                np.clip(vh, -self.F16_MAX, self.F16_MAX))
 
 
 # ------------------------------------------------- rotate-at-write variant

@@ -58,7 +58,7 @@ def _desc(**kw):
 
 def test_strerror_and_version():
     lib = _lib.load()
-    assert lib.fp4kv_abi_version() == 4
+    assert lib.fp4kv_abi_version() == 5
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.fp4kv_strerror(st)
     assert lib.fp4kv_append_workspace_bytes() >= 64 * 33 * 4   # re-rotation maxima
@@ -241,6 +241,75 @@ def test_append_noalloc_validation_before_launch():
     assert call(shots=None) == -1
     assert call(c=_desc(format_tag=7)) == -4
     assert call(c=_desc(sink_per_shot=1)) == -1
+
+
+def test_frame_position_matches_the_oracle_rule():
+    """The library's cache-relative position of every frame of every step of
+    wrapping streams equals the oracle's (ring.rel_pos, ring.pos_shot); frames
+    outside sink and window are rejected (host only, no GPU)."""
+    from oracle import ring
+    lib = _lib.load()
+    for S, W, C in ((3, 12, 3), (0, 4, 2), (1, 4, 2), (2, 6, 3), (5, 21, 3)):
+        c = _desc(sink_frames=S, window_frames=W, chunk_frames=C)
+        for f1 in range(1, 60):
+            ws = max(S, f1 - W)
+            for f in range(0, f1 + 1):
+                got = lib.fp4kv_frame_position(ctypes.byref(c), f, f1, 0)
+                if f < f1 and (f < S or f >= ws):
+                    assert got == ring.rel_pos(f, f1, S, W), (S, W, f, f1)
+                else:
+                    assert got == -1, (S, W, f, f1)
+    c = _desc(sink_frames=2, window_frames=6, chunk_frames=3, sink_per_shot=1)
+    for f1 in range(1, 40):
+        for f in range(max(0, f1 - 6), f1):
+            for fs in range(0, f + 1):
+                got = lib.fp4kv_frame_position(ctypes.byref(c), f, f1, fs)
+                want = ring.pos_shot(f, fs, f1, 2, 6)
+                if f - fs < 2 or f >= max(2, f1 - 6):
+                    assert got == want, (f, f1, fs)
+                else:
+                    assert got == -1
+    assert lib.fp4kv_frame_position(ctypes.byref(c), 5, 9, 6) == -1   # start after frame
+    assert lib.fp4kv_frame_position(ctypes.byref(_desc(format_tag=3)), 0, 1, 0) == -4
+
+
+def test_rope_frames_and_rope_append_validation_before_launch():
+    lib = _lib.load()
+    c = _desc()                                   # H2 D128 T32 C3 S3 W12, rot_dim 128
+    A, B, K, V = 0x100000, 0x200000, 0x300000, 0x400000
+    shots = (ctypes.c_int32 * 4)(0, 0, 0, 0)
+    ws = lib.fp4kv_append_workspace_bytes()
+    rf = lambda **kw: lib.fp4kv_rope_rel_frames(
+        ctypes.byref(kw.get("c", c)), kw.get("x", A), kw.get("dt", 1), kw.get("y", B),
+        kw.get("odt", 0), kw.get("f0", 0), kw.get("n", 3), kw.get("starts", None),
+        kw.get("cs", A), kw.get("npos", 15), None)
+    assert rf(x=None) == -1
+    assert rf(n=0) == -1
+    assert rf(n=65) == -1
+    assert rf(f0=-1) == -1
+    assert rf(npos=2) == -2            # position 2 is past a 2-row table
+    assert rf(cs=None) == -1
+    assert rf(y=B + 4) == -3
+    assert rf(x=A, y=A, dt=1, odt=0) == -1       # in place needs matching dtypes
+    assert rf(c=_desc(sink_per_shot=1)) == -1    # per-shot sinks need shot starts
+    assert rf(f0=0, n=16, c=_desc(window_frames=12)) == -1   # frames 0..2 before the window
+    assert rf(c=_desc(format_tag=3)) == -4
+    ra = lambda **kw: lib.fp4kv_rope_append(
+        ctypes.byref(kw.get("c", c)), kw.get("q", A), kw.get("qdt", 1), kw.get("qr", B),
+        kw.get("qrdt", 0), kw.get("k", K), kw.get("v", V), kw.get("kvdt", 1), kw.get("f0", 0),
+        kw.get("n", 3), kw.get("shots", shots), kw.get("starts", None), kw.get("cs", A),
+        kw.get("npos", 15), kw.get("ws", A), kw.get("wsb", ws), None)
+    assert ra(q=None) == -1
+    assert ra(k=None) == -1
+    assert ra(kvdt=4) == -1
+    assert ra(wsb=ws - 1) == -2
+    assert ra(ws=None) == -1
+    assert ra(qr=K) == -1              # the rotated queries would overwrite K
+    assert ra(qr=V) == -1
+    assert ra(npos=1) == -2
+    assert ra(c=_desc(format_tag=_lib.FP4KV_FORMAT_BF16_V1)) == -1
+    assert ra(c=_desc(format_tag=_lib.FP4KV_FORMAT_NVFP4_ROT_V1)) == -1
+    assert ra(f0=3, n=13) == -1        # frames 3 and 15 share a window slot
 
 
 def test_rope_validation_before_launch():

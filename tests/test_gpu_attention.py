@@ -1,10 +1,13 @@
-"""GPU parity of fp4kv_attention_chunk (with fp4kv_rope_rel on the queries
-and fp4kv_quantize_append filling the cache) against the float64 oracle.
+"""GPU parity of fp4kv_attention_chunk (with fp4kv_rope_rel_frames on the
+queries and fp4kv_quantize_append filling the cache, or both through
+fp4kv_rope_append) against the float64 oracle.
 
 Bar: max-abs error <= 1e-2 and mean-abs error <= 1e-3 of the float32-output
 kernel against the oracle on the same decoded cache (the cache bytes
 themselves are checked bit-exact on the way).  Full-size workloads compare
 sampled query rows the oracle computes one by one."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -20,13 +23,18 @@ MAX_ABS, MEAN_ABS = 1e-2, 1e-3
 
 
 def _gpu_step(api, gc, w, c, q, qb, k, kb, v, vb, out_dtype=torch.float32, append=True,
-              n_wg=0, split=True):
+              n_wg=0, split=True, fused=False):
+    """One step through the C ABI: rope_rel_frames of the queries and
+    quantize_append of the chunk, or both in one rope_append (fused)."""
     f0, n = w.chunk_frames(c)
     shots = shots_of(w, f0, n)
-    if append:
-        api.quantize_append(gc, device_tensor(k, kb), device_tensor(v, vb), f0, n, shots)
-    pos0 = api.cache_positions(w.S, w.W, f0, n)
-    qr = api.rope_rel(device_tensor(q, qb), pos0, w.T, gc.cos_sin, rot_dim=gc.rot_dim)
+    qd = device_tensor(q, qb)
+    if append and fused:
+        qr = api.rope_append(gc, qd, device_tensor(k, kb), device_tensor(v, vb), f0, n, shots)
+    else:
+        if append:
+            api.quantize_append(gc, device_tensor(k, kb), device_tensor(v, vb), f0, n, shots)
+        qr = api.rope_rel_frames(gc, qd, f0, n)
     o = api.attention_chunk(gc, qr, f0, n, shots, out_dtype=out_dtype, n_workgroups=n_wg,
                             split=split)
     torch.cuda.synchronize()
@@ -34,23 +42,36 @@ def _gpu_step(api, gc, w, c, q, qb, k, kb, v, vb, out_dtype=torch.float32, appen
 
 
 def _run_stream(w, steps, rows=None, heads=None, check_every=True, rot_dim=None, n_wg=0,
-                split=True):
+                split=True, fused=False, filler=False):
+    """Streams every chunk step 0 .. max(steps) through the GPU and checks the
+    listed steps against the oracle.  The oracle skips chunks that are
+    evicted before the next checked step (every slot then holds a frame it
+    did append).  With filler=True the GPU also streams such chunks with one
+    reused seeded chunk of data instead of their own: their bytes are
+    overwritten before any checked step reads them, so only the listed
+    steps' surviving chunks need drawing (long streams)."""
     from fp4_kv_cache_fp4kv_amd import api
     gc, oc = gpu_cache(w, rot_dim), OracleCache.for_workload(w, rot_dim)
     results = []
     checks = sorted(steps)
+    fill = None
     for c in range(max(steps) + 1):
         f0, n = w.chunk_frames(c)
-        (q, qb), (k, kb), (v, vb) = step_inputs(w, c)
         shots = shots_of(w, f0, n)
-        # the oracle skips chunks that are evicted before the next checked
-        # step (every slot then holds a frame it did append)
         nxt = min(x for x in checks if x >= c)
         f1_next = sum(w.chunk_frames(nxt))
-        if f0 < w.S or f0 + n > f1_next - w.W:
+        needed = f0 < w.S or f0 + n > f1_next - w.W
+        if needed or not filler:
+            (q, qb), (k, kb), (v, vb) = step_inputs(w, c)
+        else:
+            if fill is None or fill[0] != n:
+                fill = (n, step_inputs(w, 1))
+            (q, qb), (k, kb), (v, vb) = fill[1]
+        if needed:
             oc.append(k, v, f0, n, shots)
-        say(f"attention {w.name} step {c} frames {f0}..{f0 + n - 1}")
-        got = _gpu_step(api, gc, w, c, q, qb, k, kb, v, vb, n_wg=n_wg, split=split)
+        if c % 20 == 0 or needed:
+            say(f"attention {w.name} step {c} frames {f0}..{f0 + n - 1}")
+        got = _gpu_step(api, gc, w, c, q, qb, k, kb, v, vb, n_wg=n_wg, split=split, fused=fused)
         if c not in steps:
             continue
         assert not compare_cache(gc, oc), (w.name, c)
@@ -226,14 +247,14 @@ def test_attention_full_size_sampled(name):
     w = wl.WORKLOADS[name]
     steady = (w.S + w.W) // w.C          # first step with a full window
     steps = [0, steady - 1] if name == "l13b" else [0, steady, steady + 3]
-    _run_stream(w, steps, rows=_sample_rows(w), heads=[0, w.H // 2, w.H - 1])
+    _run_stream(w, steps, rows=_sample_rows(w), heads=[0, w.H // 2, w.H - 1], fused=True)
 
 
 def test_attention_full_size_all_rows():
     """Every query row of two heads of the 1.3B-like layer (1% outliers x20)
     at its first full-window step."""
     w = wl.L13B
-    _run_stream(w, [(w.S + w.W) // w.C - 1], heads=[0, w.H - 1])
+    _run_stream(w, [(w.S + w.W) // w.C - 1], heads=[0, w.H - 1], fused=True)
 
 
 def test_attention_full_size_without_workspace():
@@ -257,9 +278,80 @@ def test_attention_head_share_sampled(split):
 def test_attention_multishot_full_size_sampled():
     w = wl.L5B_SHOTS
     # step 6 holds frames 18..20 (the shot boundary cuts the chunk); step 26 is partial
-    _run_stream(w, [6, 7, 26], rows=_sample_rows(w, seed=1), heads=[0, w.H - 1])
+    _run_stream(w, [6, 7, 26], rows=_sample_rows(w, seed=1), heads=[0, w.H - 1], fused=True)
 
 
 def test_attention_long_stream_sampled_steps():
     w = wl.LONG
-    _run_stream(w, [0, 8, 9], rows=_sample_rows(w, seed=2), heads=[1, w.H - 2])
+    _run_stream(w, [0, 8, 9], rows=_sample_rows(w, seed=2), heads=[1, w.H - 2], fused=True)
+
+
+@pytest.mark.timeout(1200)
+def test_attention_5b_full_30_step_rollover():
+    """The 5B-like layer over its whole 30-step stream (the ring wraps 6
+    times): cache bytes bit-exact and sampled rows of two heads within the
+    bar at every step."""
+    w = wl.L5B
+    _run_stream(w, list(range(w.n_chunks)), rows=_sample_rows(w, n_rows=16, seed=7),
+                heads=[0, w.H - 1], fused=True)
+
+
+@pytest.mark.timeout(1200)
+def test_attention_long_stream_240_chunks():
+    """The long stream (W = 21, every other token kept) streamed for all 240
+    chunks; checked at steps 1, 7 (window filling), 120 and 239 (frame ids
+    in the hundreds, 30+ ring wraps)."""
+    w = wl.LONG
+    _run_stream(w, [1, 7, 120, 239], rows=_sample_rows(w, n_rows=24, seed=8),
+                heads=[0, w.H - 1], fused=True, filler=True)
+
+
+def test_attention_full_size_bf16_output_default_split():
+    """The benchmark's own launch: the 1.3B-like layer (1% outliers x20) at a
+    steady step, bf16 output with the default split over every CU.  Every
+    row of two heads: the bf16 output equals the float32 output rounded
+    once, the float32 output meets the bar, and the bf16 output meets it
+    once its own final rounding is allowed for: max-abs beyond half a bf16
+    ulp, mean-abs against the oracle rounded to bf16 (the rounding alone
+    has a mean of about 1e-3 on these outputs)."""
+    from fp4_kv_cache_fp4kv_amd import api
+    w = wl.L13B
+    steady = (w.S + w.W) // w.C - 1      # the last of its 5 steps: sink + full window
+    gc, oc = gpu_cache(w), OracleCache.for_workload(w)
+    for c in range(steady + 1):
+        f0, n = w.chunk_frames(c)
+        (q, qb), (k, kb), (v, vb) = step_inputs(w, c)
+        shots = shots_of(w, f0, n)
+        oc.append(k, v, f0, n, shots)
+        say(f"bf16-output l13b step {c}")
+        qr = api.rope_append(gc, device_tensor(q, qb), device_tensor(k, kb),
+                             device_tensor(v, vb), f0, n, shots)
+    o16 = api.attention_chunk(gc, qr, f0, n, shots, out_dtype=torch.bfloat16)
+    o32 = api.attention_chunk(gc, qr, f0, n, shots, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert not compare_cache(gc, oc)
+    hs = [0, w.H - 1]
+    g16 = o16.float().cpu().numpy()[:, hs].astype(np.float64)
+    g32 = o32.cpu().numpy()[:, hs].astype(np.float64)
+    ref = oc.attention(q, f0, n, shots, heads=hs)
+    half_ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(g16), 1e-38))) - 8)
+    assert np.all(np.abs(g16 - g32) <= half_ulp * (1 + 1e-6) + 1e-38)
+    mx32, mn32 = err_stats(g32, ref)
+    mx16, mn16 = err_stats(g16, ref)
+    excess = (np.abs(g16 - ref) - half_ulp).max()
+    # against the oracle rounded to bf16 the same way, the rounding itself
+    # cancels wherever both round alike
+    ref16 = wl.bf16_round(ref.astype(np.float32))[0].astype(np.float64)
+    mn16r = float(np.abs(g16 - ref16).mean())
+    say(f"  f32 max-abs {mx32:.3e} mean {mn32:.3e}; bf16 raw max-abs {mx16:.3e} "
+        f"mean {mn16:.3e}, beyond its rounding {excess:.3e}, mean vs rounded oracle {mn16r:.3e}")
+    assert mx32 <= MAX_ABS and mn32 <= MEAN_ABS
+    assert excess <= MAX_ABS and mn16r <= MEAN_ABS
+
+
+def test_attention_full_size_second_seed():
+    """The 1.3B-like layer with another seed (outliers land elsewhere):
+    sampled rows of every head at the first full-window step."""
+    w = dataclasses.replace(wl.L13B, name="l13b_seed12", seed=12)
+    _run_stream(w, [(w.S + w.W) // w.C - 1], rows=_sample_rows(w, n_rows=32, seed=9),
+                fused=True)

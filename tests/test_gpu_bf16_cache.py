@@ -44,8 +44,7 @@ def _run(w, steps, rows=None, heads=None):
         oc.append(k, v, f0, n, shots)
         say(f"bf16 cache {w.name} step {c}")
         api.quantize_append(gc, device_tensor(k, kb), device_tensor(v, vb), f0, n, shots)
-        qr = api.rope_rel(device_tensor(q, qb), api.cache_positions(w.S, w.W, f0, n), w.T,
-                          gc.cos_sin)
+        qr = api.rope_rel_frames(gc, device_tensor(q, qb), f0, n)
         o = api.attention_chunk(gc, qr, f0, n, shots, out_dtype=torch.float32)
         torch.cuda.synchronize()
         if c not in steps:
@@ -110,10 +109,7 @@ def test_bf16_cache_per_shot_sinks_cuts_inside_chunks():
         api.quantize_append(gc, device_tensor(k, kb), device_tensor(v, vb), f0, n, shots,
                             shot_starts=fss)
         qd = device_tensor(q, qb)
-        for j in range(n):
-            rows = slice(j * w.T, (j + 1) * w.T)
-            api.rope_rel(qd[rows], api.frame_position(w.S, w.W, f0 + j, f0 + n, fss[j]), w.T,
-                         gc.cos_sin, out=qrot[rows])
+        api.rope_rel_frames(gc, qd, f0, n, shot_starts=fss, out=qrot[:n * w.T])
         o = api.attention_chunk(gc, qrot[:n * w.T], f0, n, shots, out_dtype=torch.float32)
         torch.cuda.synchronize()
         assert not _compare(gc, oc), (c, _compare(gc, oc))

@@ -183,8 +183,7 @@ def test_bulk_reappend_kv_recache():
         assert not compare_cache(gc, oc), (f0, n)
     q, qb = wl.draw(w, w.n_chunks - 1, wl.Q_ID)
     f0 = f1 - w.C
-    qr = api.rope_rel(device_tensor(q, qb), api.cache_positions(w.S, w.W, f0, w.C), w.T,
-                      gc.cos_sin)
+    qr = api.rope_rel_frames(gc, device_tensor(q, qb), f0, w.C)
     o = api.attention_chunk(gc, qr, f0, w.C, [0] * w.C, out_dtype=torch.float32)
     torch.cuda.synchronize()
     mx, mn = err_stats(o.cpu().numpy(), oc.attention(q, f0, w.C, [0] * w.C))

@@ -1,0 +1,98 @@
+"""GPU checks of the library-computed positions and of the fused step
+prologue, through the C ABI:
+
+  * fp4kv_rope_rel_frames rotates each frame by the oracle's cache-relative
+    position (also across shot cuts with per-shot sinks, where positions are
+    not consecutive): bit for bit what fp4kv_rope_rel gives with those
+    positions, and within float32 error of the oracle's float64 rotation;
+  * fp4kv_rope_append (the queries' rotation and the append in two kernels)
+    leaves the same cache bytes and rotated queries as the separate calls,
+    step after step, on the small streams and on the full-size layers.
+"""
+import numpy as np
+import pytest
+import torch
+
+from fp4_kv_cache_fp4kv_amd import workloads as wl
+from oracle import ring, rope
+from streams import CACHE_FIELDS, device_tensor, say, shots_of, step_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _shot_start(w, f):
+    s0 = w.shot_of(f)
+    while f > 0 and w.shot_of(f - 1) == s0:
+        f -= 1
+    return f
+
+
+def _bytes(gc):
+    v = gc.views()
+    return {n: v[n].cpu().numpy().tobytes() for n in CACHE_FIELDS if n in v}
+
+
+@pytest.mark.parametrize("per_shot", [False, True])
+def test_rope_rel_frames_uses_the_oracle_positions(per_shot):
+    from fp4_kv_cache_fp4kv_amd import api
+    w = wl.Workload("rf", H=3, D=128, T=24, C=3, S=2, W=6, n_frames=22, seed=71, shot_len=5)
+    gc = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, rot_dim=96, sink_per_shot=per_shot)
+    for c in range(w.n_chunks):
+        f0, n = w.chunk_frames(c)
+        f1 = f0 + n
+        (q, qb), _, _ = step_inputs(w, c)
+        fss = [_shot_start(w, f) for f in range(f0, f1)] if per_shot else None
+        pos = [ring.pos_shot(f, fss[j], f1, w.S, w.W) if per_shot else ring.rel_pos(f, f1, w.S, w.W)
+               for j, f in enumerate(range(f0, f1))]
+        say(f"rope_rel_frames step {c} positions {pos}")
+        qd = device_tensor(q, qb)
+        got = api.rope_rel_frames(gc, qd, f0, n, shot_starts=fss)
+        ref = torch.empty_like(got)
+        for j in range(n):
+            r = slice(j * w.T, (j + 1) * w.T)
+            api.rope_rel(qd[r], pos[j], w.T, gc.cos_sin, rot_dim=96, out=ref[r])
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), c
+        exact = rope.rotate(q, np.repeat(pos, w.T)[:, None], 96)
+        mag = np.abs(q).astype(np.float64)
+        assert np.all(np.abs(got.cpu().numpy() - exact) <= 2.0 ** -20 * (mag + np.roll(mag, 1, -1)
+                                                                          + np.roll(mag, -1, -1)) + 1e-37)
+
+
+def _prologue_stream(w, steps, per_shot=False, check=None):
+    """Separate calls into cache A, rope_append into cache B; the bytes of
+    both caches and both rotated queries must be identical at every step."""
+    from fp4_kv_cache_fp4kv_amd import api
+    a = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride, sink_per_shot=per_shot)
+    b = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride, sink_per_shot=per_shot)
+    for c in range(steps):
+        f0, n = w.chunk_frames(c)
+        (q, qb), (k, kb), (v, vb) = step_inputs(w, c)
+        shots = shots_of(w, f0, n)
+        fss = [_shot_start(w, f) for f in range(f0, f0 + n)] if per_shot else None
+        say(f"rope_append {w.name} step {c} frames {f0}..{f0 + n - 1}")
+        qd, kd, vd = device_tensor(q, qb), device_tensor(k, kb), device_tensor(v, vb)
+        api.quantize_append(a, kd, vd, f0, n, shots, shot_starts=fss)
+        qa = api.rope_rel_frames(a, qd, f0, n, shot_starts=fss)
+        qb_ = api.rope_append(b, qd, kd, vd, f0, n, shots, shot_starts=fss)
+        torch.cuda.synchronize()
+        if check is None or c in check:
+            assert torch.equal(qa.view(torch.int32), qb_.view(torch.int32)), (w.name, c)
+            ba, bb = _bytes(a), _bytes(b)
+            for name in ba:
+                assert ba[name] == bb[name], (w.name, c, name)
+
+
+def test_rope_append_equals_separate_calls_small():
+    _prologue_stream(wl.TINY, wl.TINY.n_chunks)
+    w = wl.Workload("tiny_mix", H=3, D=64, T=24, C=3, S=2, W=6, n_frames=20, seed=21,
+                    dtype="bf16", token_stride=2, shot_len=5)
+    _prologue_stream(w, w.n_chunks)
+    _prologue_stream(w, w.n_chunks, per_shot=True)
+
+
+@pytest.mark.parametrize("name", ["l13b", "long", "l5b_shots"])
+def test_rope_append_equals_separate_calls_full_size(name):
+    w = wl.WORKLOADS[name]
+    steps = 8 if name == "long" else min(w.n_chunks, (w.S + w.W) // w.C + 1)
+    _prologue_stream(w, steps, per_shot=name == "l5b_shots", check={0, steps - 1})

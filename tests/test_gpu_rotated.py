@@ -56,12 +56,10 @@ def _run(w, steps, rot_dim=None, per_shot=False, rows=None, heads=None, fused=Fa
                                         shot_starts=fss)
         else:
             api.rerotate_window(gc, f0, f1)
-        for j in range(n):   # per frame: positions jump at a cut with per-shot sinks
-            pos = api.frame_position(w.S, w.W, f0 + j, f1, fss[j] if per_shot else None)
-            r = slice(j * w.T, (j + 1) * w.T)
-            if not fused:
-                api.rope_rel(kd[r], pos, w.T, gc.cos_sin, rot_dim=gc.rot_dim, out=krot[r])
-            api.rope_rel(qd[r], pos, w.T, gc.cos_sin, rot_dim=gc.rot_dim, out=qrot[r])
+        # per frame: positions jump at a cut with per-shot sinks
+        if not fused:
+            api.rope_rel_frames(gc, kd, f0, n, shot_starts=fss, out=krot[:n * w.T])
+        api.rope_rel_frames(gc, qd, f0, n, shot_starts=fss, out=qrot[:n * w.T])
         if not fused:   # values go in as float32 (bf16 inputs are exact in float32)
             api.quantize_append(gc, krot[:n * w.T], device_tensor(v, None), f0, n, shots,
                                 shot_starts=fss)

@@ -37,10 +37,9 @@ def _run(w, steps, rows=None, heads=None):
         api.quantize_append(gc, device_tensor(k, kb), device_tensor(v, vb), f0, n, shots,
                             shot_starts=fss)
         qd = device_tensor(q, qb)
-        for j in range(n):   # positions need not be consecutive across a cut
-            pos = api.frame_position(w.S, w.W, f0 + j, f0 + n, fss[j])
-            rows_j = slice(j * w.T, (j + 1) * w.T)
-            api.rope_rel(qd[rows_j], pos, w.T, gc.cos_sin, out=qrot[rows_j])
+        # positions need not be consecutive across a cut; the library
+        # computes each frame's
+        api.rope_rel_frames(gc, qd, f0, n, shot_starts=fss, out=qrot[:n * w.T])
         o = api.attention_chunk(gc, qrot[:n * w.T], f0, n, shots, out_dtype=torch.float32)
         torch.cuda.synchronize()
         if c not in steps:

@@ -288,3 +288,29 @@ def test_reappend_is_idempotent():
         cache.append(k, v, f0, n, [0] * n)
         for name in ("k_codes", "v_codes", "k_scales", "v_scales", "k_tscale", "slot_frame"):
             assert np.array_equal(getattr(cache, name), getattr(snap, name))
+
+
+def test_query_saturation_to_the_f16_range():
+    """Queries beyond the f16 range: a rotary pair whose norm exceeds 65504
+    keeps its direction at norm 65504, an element past rot_dim is clamped,
+    and in-range queries are untouched (closed forms)."""
+    oc = OracleCache(1, 64, 2, 1, 1, 4, rot_dim=32)
+    q = np.zeros((2, 1, 64), np.float32)
+    q[0, 0, 0], q[0, 0, 1] = 3.0e5, 4.0e5          # norm 5e5 -> 65504, direction (0.6, 0.8)
+    q[0, 0, 40] = -1.0e6                           # past rot_dim: clamped
+    q[1, 0, :] = 1.5                               # in range
+    y = oc.rope_queries(q, 0, 1)                   # frame 0, position 0: no turn
+    assert np.isclose(np.hypot(y[0, 0, 0], y[0, 0, 1]), 65504.0, rtol=1e-12)
+    assert np.isclose(y[0, 0, 0] / y[0, 0, 1], 0.75, rtol=1e-12)
+    assert y[0, 0, 40] == -65504.0
+    assert np.array_equal(y[1, 0], np.full(64, 1.5))
+    # a turned pair has the same norm, so saturating before or after the
+    # rotation gives the same query
+    y3 = oc.rope_queries(q, 3, 1)                  # frame 3 at position 3
+    assert np.isclose(np.hypot(y3[0, 0, 0], y3[0, 0, 1]), 65504.0, rtol=1e-12)
+
+
+def test_caller_scale_guard():
+    assert OracleCache.caller_scale(0.5) == np.float32(0.5)
+    for bad in (0.0, -1.0, np.inf, np.nan):
+        assert OracleCache.caller_scale(bad) == np.float32(1.0)

@@ -61,3 +61,17 @@ def test_bf16_cache_full_window_equals_dense_attention():
             ref = torch.nn.functional.scaled_dot_product_attention(
                 qr, kr, vt, attn_mask=torch.from_numpy(mask)[None, None])[0, 0].numpy()
             assert np.allclose(out[:, h], ref, atol=1e-10), (step, h)
+
+
+def test_operands_saturate_to_the_f16_range():
+    """Stored bf16 values beyond the f16 range keep their bits in the cache
+    and saturate to +-65504 only where attention reads them."""
+    from oracle.stream import OracleCacheBF16
+    c = OracleCacheBF16(1, 64, 32, 1, 1, 2)
+    k = np.full((32, 1, 64), 1.0e6, np.float32)
+    v = np.full((32, 1, 64), -2.0e5, np.float32)
+    c.append(k, v, 0, 1, [0])
+    kh, vh = c.decode_slot(0)
+    assert kh.max() > 65504.0 and vh.min() < -65504.0
+    ko, vo = c.operands(kh, vh)
+    assert ko.max() == 65504.0 and vo.min() == -65504.0
