@@ -53,6 +53,8 @@ namespace {
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;               // two groups of 4, one wave of each per SIMD
 constexpr int kThreads = kWaves * 64;
@@ -394,15 +396,9 @@ __device__ __forceinline__ void scores(f32x16 (&s)[2], const uint16_t (*kt)[D + 
   }
 }
 
-// P = exp2(s * cf - m) rounded to f16 as four P^T operands of 16 keys, and
-// l += sum of P.
+// P = exp2(s * cf - m) rounded to f16 as four P^T operands of 16 keys.
 __device__ __forceinline__ void softmax_weights(const f32x16 (&s)[2], float cf, float m,
-                                                float &l, f16x8 (&pb)[4]) {
-  // The row sum adds the rounded weights, converted back to float32, in 8
-  // independent partial sums (a packed f16 dot product is a slow
-  // instruction here and made the whole kernel 7% slower; a mixed-precision
-  // FMA per weight made the compiler spill 89 registers).
-  float lp[2][4] = {};
+                                                f16x8 (&pb)[4]) {
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -413,13 +409,10 @@ __device__ __forceinline__ void softmax_weights(const f32x16 (&s)[2], float cf, 
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b][8 * t2 + 2 * e], cf, -m));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b][8 * t2 + 2 * e + 1], cf, -m));
         const f16x2 ph = {(_Float16)p0, (_Float16)p1};
-        lp[b][e] += (float)ph[0] + (float)ph[1];
         w[e] = bits(ph);
       }
       pb[2 * b + t2] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
     }
-  l += ((lp[0][0] + lp[0][1]) + (lp[0][2] + lp[0][3])) +
-       ((lp[1][0] + lp[1][1]) + (lp[1][2] + lp[1][3]));
 }
 
 // V^T operands of a tile for this wave: slice t4 (16 keys), block db (32
@@ -436,19 +429,29 @@ __device__ __forceinline__ void read_v_operands(f16x8 (&va)[D / 8],
       va[t4 * DB + db] = as_f16x8(*(const uint4 *)&vt[32 * db + n][16 * t4 + 8 * hf]);
 }
 
-// O^T += V^T P^T over the four slices of 16 keys of a tile.  The compiler
-// interleaves the dequantization that follows with these MFMAs by itself
-// (a fixed 1 MFMA : 3 VALU pattern measured 1% slower).
+// O^T += V^T P^T over the four slices of 16 keys of a tile, and this lane's
+// share of l += sum of P.  The row sum adds exactly the rounded weights the
+// PV product uses (products with 1 are exact, sums in float32).  On the
+// VALU it cost about 100 instructions per tile (the compiler rounds each
+// weight a second time for it); here it costs eight small MFMAs.
 template <int D>
-__device__ __forceinline__ void accumulate_pv(f32x16 (&o)[D / 32], const f16x8 (&va)[D / 8],
-                                              const f16x8 (&pb)[4]) {
+__device__ __forceinline__ void accumulate_pv(f32x16 (&o)[D / 32], f32x4 &lsum,
+                                              const f16x8 (&va)[D / 8], const f16x8 (&pb)[4]) {
   constexpr int DB = D / 32;
+  const f16x4 ones = {1, 1, 1, 1};
 #pragma unroll
-  for (int t4 = 0; t4 < 4; ++t4)
+  for (int t4 = 0; t4 < 4; ++t4) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       o[db] = mfma32(va[t4 * DB + db], pb[t4], o[db]);
     }
+    // Row sum on the matrix cores: 16 blocks of 4x4x4 with A all ones give
+    // every lane the float32 sum of its own four weights of the operand.
+    lsum = __builtin_amdgcn_mfma_f32_4x4x4f16(
+        ones, __builtin_shufflevector(pb[t4], pb[t4], 0, 1, 2, 3), lsum, 0, 0, 0);
+    lsum = __builtin_amdgcn_mfma_f32_4x4x4f16(
+        ones, __builtin_shufflevector(pb[t4], pb[t4], 4, 5, 6, 7), lsum, 0, 0, 0);
+  }
 }
 
 // Masks the scores of keys at or past nval and of rows that do not see the
@@ -504,14 +507,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Workgroup barrier for a wave that has written nothing to LDS since the
-// last barrier: its own LDS reads may still be in flight (their data is not
-// overwritten until several phases later).  The memory clobber keeps the
-// compiler from moving memory accesses across it.
-__device__ __forceinline__ void barrier_reads_in_flight() {
-  asm volatile("s_barrier" ::: "memory");
-}
-
 // The kernel's argument block (a single AttnParams at offset 0), read
 // through a pointer the compiler cannot see through.
 __device__ __forceinline__ const AttnParams &opaque_params() {
@@ -552,16 +547,18 @@ __device__ __forceinline__ int walk_index(unsigned long long visible, int x, int
 // each group on every SIMD; both groups walk the same tiles for different
 // query rows, offset by one phase.  Phases end at workgroup barriers, and in
 // every phase one group issues MFMAs while the other does the softmax:
-//   MFMA phase of step t:  O += V(t-1) P(t-1), S(t) = K(t) Q'^T, and in the
-//                          shadow of these MFMAs one half of a later tile
-//                          dequantized (group 0: V of tile t+1, group 1: K of
-//                          tile t+1) and the codes of its next half loaded;
-//   VALU phase of step t:  mask, row max and rescale of S(t), P(t) and l; the
-//                          queries turned into the frame of tile t+1.
+//   MFMA phase of step t:  O += V(t-1) P(t-1) and l += sum of P(t-1), then
+//                          S(t) = K(t) Q'^T;
+//   VALU phase of step t:  mask, row max and rescale of S(t), and P(t); the
+//                          queries turned into the frame of tile t+1; one
+//                          half of tile t+2 dequantized (group 0: V, group 1:
+//                          K) and the codes of its next half loaded; the V
+//                          operands of tile t read.
 // Group 0 runs MFMA phases on even phases 2t, group 1 on odd phases 2t+1
-// after an empty opening phase.  K(t) is written in phase 2t-1 and read in
-// phases 2t and 2t+1 (2 buffers); V(t) is written in phase 2t-2 and read in
-// phases 2t+2 and 2t+3 (3 buffers).
+// after an empty opening phase.  Tiles 0 and 1 are dequantized before phase
+// 0.  K(t) is written in phase 2t-2 and read in phases 2t and 2t+1 (2
+// buffers); V(t) is written in phase 2t-3 and read in phases 2t+1 and 2t+2
+// (3 buffers).  Every phase ends at an LDS barrier.
 template <int D, bool OUT_F32, bool BF16KV>
 __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
   constexpr int KS = D / 16;   // k-steps of S^T over d
@@ -688,7 +685,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int j = 0; j < 16; ++j) oacc[b][j] = 0.0f;
-    float m_run = -1.0e30f, l_part = 0.0f, gv_last = 1.0f;
+    float m_run = -1.0e30f, gv_last = 1.0f;
+    f32x4 lsum = {};   // element 0: this lane's share of the row sum
 
     if (n_total > 0) {
       const int krow = krow_phys(sigma(n));   // + 32 b for key block b
@@ -817,10 +815,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
           load_half();
         };
 
-        // ---- prologue: tile 0 dequantized, the codes of tile 1 loading
+        // ---- prologue: tiles 0 and 1 dequantized, the codes of tile 2 loading
         load_half();
         dequant_next();
-        lds_barrier();   // tile 0, the turn table and the frame list are in LDS
+        dequant_next();
+        lds_barrier();   // tiles 0 and 1, the turn table and the frame list are in LDS
 
         if constexpr (L) turn_queries(fa, true);
         load_frame(fa);
@@ -841,7 +840,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
             const float m_new = fmaxf(m_run, tmax);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
-            l_part *= alpha;
+            lsum[0] *= alpha;
             factor *= alpha;
             scale_o = true;
           }
@@ -851,11 +850,12 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     #pragma unroll
               for (int j = 0; j < 16; ++j) oacc[b][j] *= factor;
           }
-          softmax_weights(s, f_cf, m_run, l_part, pb);
+          softmax_weights(s, f_cf, m_run, pb);
         };
 
-        // VALU phase of step t: softmax of tile t, then the queries turned into
-        // the frame of tile t+1
+        // VALU phase of step t: softmax of tile t, the queries turned into the
+        // frame of tile t+1, the group's half of tile t+2 dequantized, and the
+        // V operands of tile t read
         auto valu_phase = [&](int t) __attribute__((always_inline)) {
           if constexpr (L) {
             if (t < n_total) {
@@ -873,19 +873,18 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
             }
             ct = cn;
           }
-          // V operands of tile t for the next MFMA phase (V(t) has been in LDS
-          // since phase 2t-2 and is overwritten only in phase 2t+4)
+          // The group's half of tile t + 2, then the V operands of tile t for
+          // the next MFMA phase
+          dequant_next();
           if constexpr (L) read_v_operands<D>(va, sm.vt[t % kVBufs], n, hf);
         };
 
-        // MFMA phase of step t, with the dequantization of the group's next
-        // half tile in the shadow of the MFMAs.  P is consumed first and S
-        // produced last, which keeps the registers of P, the dequantization and
-        // S from being live at the same time.
+        // MFMA phase of step t: PV of tile t - 1, then S of tile t.  It issues
+        // matrix work only, at raised priority; the dequantization runs in the
+        // VALU phase, where the other group's MFMAs leave issue cycles free.
         auto mfma_phase = [&](int t, auto has_pv, auto has_s) __attribute__((always_inline)) {
           __builtin_amdgcn_s_setprio(1);
-          if constexpr (L && decltype(has_pv)::value) accumulate_pv<D>(oacc, va, pb);
-          dequant_next();
+          if constexpr (L && decltype(has_pv)::value) accumulate_pv<D>(oacc, lsum, va, pb);
           if constexpr (L && decltype(has_s)::value)
             scores<D>(s, sm.kh[t % kKBufs], krow, hf, qhi, qlo);
           __builtin_amdgcn_s_setprio(0);
@@ -895,11 +894,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
         if (G) lds_barrier();   // group 1's opening phase
         mfma_phase(0, BoolC<false>(), BoolC<true>());
         valu_phase(0);
-        barrier_reads_in_flight();
+        lds_barrier();
         for (int t = 1; t < n_total; ++t) {
           mfma_phase(t, BoolC<true>(), BoolC<true>());
           valu_phase(t);
-          barrier_reads_in_flight();
+          lds_barrier();
         }
         mfma_phase(n_total, BoolC<true>(), BoolC<false>());
         if (!G) lds_barrier();   // group 0's closing phase
@@ -916,7 +915,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     }
 
     // ---- epilogue: O = g_v * acc / l, g_v of the last frame walked
-    const float l = halves_sum(l_part);
+    const float l = halves_sum(lsum[0]);
     auto store_out = [&](float inv) __attribute__((always_inline)) {
       if (!row_ok) return;
       const long long obase = ((long long)my_row * p.H + head) * D;
