@@ -797,7 +797,10 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
         constexpr bool L = decltype(ltag)::value;
         typename RawOf<G, BF16KV>::type raw;
         Cursor cd = {fa, ta, 0};
-        SlotRes res = slot_resources<D, BF16KV>(p, head, sm.fl_slot[fa]);   // frame of cd
+        // (the slot index is wave-uniform; read as such, the descriptors sit in
+        // scalar registers and the tile loads need no waterfall loop)
+        SlotRes res = slot_resources<D, BF16KV>(
+            p, head, __builtin_amdgcn_readfirstlane(sm.fl_slot[fa]));   // frame of cd
         auto load_half = [&]() __attribute__((always_inline)) {
           if constexpr (G) load_k<D>(res, cd.tt * kBN, lt, raw);
           else load_v<D>(res, p.Tv, cd.tt * kBN, lt, raw);
@@ -810,7 +813,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
           else dequant_v<D>(raw, lt, sm.vt[cd.i % kVBufs]);
           Cursor nx = advance(cd);
           nx.i = cd.i + 1;
-          if (nx.fi != cd.fi) res = slot_resources<D, BF16KV>(p, head, sm.fl_slot[nx.fi]);
+          if (nx.fi != cd.fi)
+            res = slot_resources<D, BF16KV>(p, head, __builtin_amdgcn_readfirstlane(sm.fl_slot[nx.fi]));
           cd = nx;
           load_half();
         };
