@@ -302,26 +302,18 @@ __device__ __forceinline__ void dequant_v(const RawV &r, int lt, uint16_t (*vt)[
   if (lt < 2 * D) {
     const int rp = lt >> 2, kg = lt & 3;
     const uint32_t sw[4] = {r.vs.x, r.vs.y, r.vs.z, r.vs.w};
-    f16x2 sc[8];   // scales of token pairs (2j, 2j+1)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      sc[2 * w] = fp8x2<false>(sw[w]);
-      sc[2 * w + 1] = fp8x2<true>(sw[w]);
-    }
+    for (int w = 0; w < 2; ++w) {   // tokens 8 w .. 8 w + 7 of both dimensions
+      // scales of the token pairs (8 w + 2 j, 8 w + 2 j + 1)
+      const f16x2 sc[4] = {fp8x2<false>(sw[2 * w]), fp8x2<true>(sw[2 * w]),
+                           fp8x2<false>(sw[2 * w + 1]), fp8x2<true>(sw[2 * w + 1])};
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const uint32_t cw[2] = {r.vc[rr].x, r.vc[rr].y};
-      uint32_t o[8];
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        o[4 * w + 0] = bits(fp4x2<0>(cw[w]) * sc[4 * w + 0]);
-        o[4 * w + 1] = bits(fp4x2<1>(cw[w]) * sc[4 * w + 1]);
-        o[4 * w + 2] = bits(fp4x2<2>(cw[w]) * sc[4 * w + 2]);
-        o[4 * w + 3] = bits(fp4x2<3>(cw[w]) * sc[4 * w + 3]);
+      for (int rr = 0; rr < 2; ++rr) {
+        const uint32_t cw = w == 0 ? r.vc[rr].x : r.vc[rr].y;
+        uint4 *dst = (uint4 *)&vt[2 * rp + rr][16 * kg];
+        dst[w] = make_uint4(bits(fp4x2<0>(cw) * sc[0]), bits(fp4x2<1>(cw) * sc[1]),
+                            bits(fp4x2<2>(cw) * sc[2]), bits(fp4x2<3>(cw) * sc[3]));
       }
-      uint4 *dst = (uint4 *)&vt[2 * rp + rr][16 * kg];
-      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
     }
   }
 }
@@ -547,12 +539,12 @@ __device__ __forceinline__ int walk_index(unsigned long long visible, int x, int
 // each group on every SIMD; both groups walk the same tiles for different
 // query rows, offset by one phase.  Phases end at workgroup barriers, and in
 // every phase one group issues MFMAs while the other does the softmax:
-//   MFMA phase of step t:  O += V(t-1) P(t-1) and l += sum of P(t-1), then
-//                          S(t) = K(t) Q'^T;
+//   MFMA phase of step t:  O += V(t-1) P(t-1) and l += sum of P(t-1), the
+//                          codes of one half of tile t+2 (group 0: V, group
+//                          1: K) loaded, then S(t) = K(t) Q'^T;
 //   VALU phase of step t:  mask, row max and rescale of S(t), and P(t); the
-//                          queries turned into the frame of tile t+1; one
-//                          half of tile t+2 dequantized (group 0: V, group 1:
-//                          K) and the codes of its next half loaded; the V
+//                          queries turned into the frame of tile t+1; the
+//                          group's half of tile t+2 dequantized; the V
 //                          operands of tile t read.
 // Group 0 runs MFMA phases on even phases 2t, group 1 on odd phases 2t+1
 // after an empty opening phase.  Tiles 0 and 1 are dequantized before phase
@@ -805,12 +797,17 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
           if constexpr (G) load_k<D>(res, cd.tt * kBN, lt, raw);
           else load_v<D>(res, p.Tv, cd.tt * kBN, lt, raw);
         };
-        // Dequantizes the half tile cd.i into its buffer and loads the codes of
-        // the next one.  Past the end of the walk the loads repeat the last
-        // tile and the dequantized copies land in buffers no phase reads.
-        auto dequant_next = [&]() __attribute__((always_inline)) {
-          if constexpr (G) dequant_k<D>(raw, lt, sm.kh[cd.i % kKBufs]);
-          else dequant_v<D>(raw, lt, sm.vt[cd.i % kVBufs]);
+        // Dequantizes the half tile cd.i into its buffer (tiles past the end
+        // of the walk are never read and are skipped).
+        auto dequant_tile = [&]() __attribute__((always_inline)) {
+          if (cd.i < n_total) {
+            if constexpr (G) dequant_k<D>(raw, lt, sm.kh[cd.i % kKBufs]);
+            else dequant_v<D>(raw, lt, sm.vt[cd.i % kVBufs]);
+          }
+        };
+        // Moves cd to the next tile and loads its codes (past the end of the
+        // walk the loads repeat the last tile).
+        auto next_codes = [&]() __attribute__((always_inline)) {
           Cursor nx = advance(cd);
           nx.i = cd.i + 1;
           if (nx.fi != cd.fi)
@@ -819,10 +816,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
           load_half();
         };
 
-        // ---- prologue: tiles 0 and 1 dequantized, the codes of tile 2 loading
+        // ---- prologue: tiles 0 and 1 dequantized
         load_half();
-        dequant_next();
-        dequant_next();
+        dequant_tile();
+        next_codes();
+        dequant_tile();
         lds_barrier();   // tiles 0 and 1, the turn table and the frame list are in LDS
 
         if constexpr (L) turn_queries(fa, true);
@@ -877,9 +875,9 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
             }
             ct = cn;
           }
-          // The group's half of tile t + 2, then the V operands of tile t for
-          // the next MFMA phase
-          dequant_next();
+          // The group's half of tile t + 2 (its codes were loaded in the MFMA
+          // phase), then the V operands of tile t for the next MFMA phase
+          dequant_tile();
           if constexpr (L) read_v_operands<D>(va, sm.vt[t % kVBufs], n, hf);
         };
 
@@ -889,6 +887,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
         auto mfma_phase = [&](int t, auto has_pv, auto has_s) __attribute__((always_inline)) {
           __builtin_amdgcn_s_setprio(1);
           if constexpr (L && decltype(has_pv)::value) accumulate_pv<D>(oacc, lsum, va, pb);
+          next_codes();   // of tile t + 2
           if constexpr (L && decltype(has_s)::value)
             scores<D>(s, sm.kh[t % kKBufs], krow, hf, qhi, qlo);
           __builtin_amdgcn_s_setprio(0);
