@@ -62,7 +62,7 @@ constexpr int kBM = kWaves * 32;        // query rows per workgroup
 constexpr int kBN = 64;                 // keys per tile
 constexpr int kPad = 8;                 // f16 elements of padding per LDS row
 constexpr int kXcds = 8;                // accelerator complex dies of MI355X
-constexpr int kKBufs = 2, kVBufs = 3;   // dequantized K and V tiles in LDS
+constexpr int kKBufs = 2, kVBufs = 4;   // dequantized K and V tiles in LDS
 
 // Buffer resource (gfx9 format) over `bytes` bytes at `base`: loads at
 // offsets past the end return zero instead of touching memory.
@@ -499,6 +499,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Barrier at the end of a VALU phase of a wave that read V operands: its LDS
+// writes (the dequantized tile, issued before its D/8 >= 8 V-operand reads)
+// are complete, and up to 8 of the reads stay in flight.  LDS operations of
+// a wave complete in order, so at most 8 outstanding means that everything
+// issued before the last 8 reads is done.  The reads' buffer is next written
+// three phases later.
+__device__ __forceinline__ void barrier_v_reads_in_flight() {
+  asm volatile("s_waitcnt lgkmcnt(8)\n\ts_barrier" ::: "memory");
+}
+
 // The kernel's argument block (a single AttnParams at offset 0), read
 // through a pointer the compiler cannot see through.
 __device__ __forceinline__ const AttnParams &opaque_params() {
@@ -549,8 +559,10 @@ __device__ __forceinline__ int walk_index(unsigned long long visible, int x, int
 // Group 0 runs MFMA phases on even phases 2t, group 1 on odd phases 2t+1
 // after an empty opening phase.  Tiles 0 and 1 are dequantized before phase
 // 0.  K(t) is written in phase 2t-2 and read in phases 2t and 2t+1 (2
-// buffers); V(t) is written in phase 2t-3 and read in phases 2t+1 and 2t+2
-// (3 buffers).  Every phase ends at an LDS barrier.
+// buffers); V(t) is written in phase 2t-3 and read in phases 2t+1 and 2t+2,
+// where the reads may stay in flight into the next phase (4 buffers: the
+// buffer is written again in phase 2t+5).  Every phase ends at a barrier
+// after the phase's LDS writes are complete.
 template <int D, bool OUT_F32, bool BF16KV>
 __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
   constexpr int KS = D / 16;   // k-steps of S^T over d
@@ -895,13 +907,17 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
         };
 
         if (G) lds_barrier();   // group 1's opening phase
+        auto valu_barrier = [&]() __attribute__((always_inline)) {
+          if constexpr (L) barrier_v_reads_in_flight();
+          else lds_barrier();   // no V reads follow the LDS writes
+        };
         mfma_phase(0, BoolC<false>(), BoolC<true>());
         valu_phase(0);
-        lds_barrier();
+        valu_barrier();
         for (int t = 1; t < n_total; ++t) {
           mfma_phase(t, BoolC<true>(), BoolC<true>());
           valu_phase(t);
-          lds_barrier();
+          valu_barrier();
         }
         mfma_phase(n_total, BoolC<true>(), BoolC<false>());
         if (!G) lds_barrier();   // group 0's closing phase
