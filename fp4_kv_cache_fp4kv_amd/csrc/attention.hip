@@ -10,7 +10,7 @@
 //   * a row block is 256 query rows of one head, held by one workgroup of 8
 //     waves x 32 rows (one workgroup per CU, two waves per SIMD);
 //   * the keys of all visible frames of a row block are walked as one
-//     sequence of 64-key tiles, dequantized into LDS (2 K and 3 V buffers).
+//     sequence of 64-key tiles, dequantized into LDS (2 K and 4 V buffers).
 //     Dequantization is exact: E2M1 x E4M3 has at most 6 significant bits
 //     and lies in [2^-10, 2688], so it fits f16; the hardware converts two
 //     FP4 codes to f16 (scale 1) and one packed f16 multiply applies the
@@ -21,8 +21,8 @@
 //   * O^T += V^T P^T, with P taken straight from the score registers and V
 //     read dimension-major, as the cache stores it;
 //   * ping-pong schedule: the waves form two groups with one wave of each
-//     on every SIMD, and while one group issues MFMAs (with the dequantization
-//     of a later tile in their shadow) the other does the softmax;
+//     on every SIMD, and while one group issues MFMAs the other does the
+//     softmax and dequantizes its half of a later tile;
 //   * split schedule: the key tiles of all row blocks are cut into one
 //     contiguous range per workgroup; a row block shared by two or more
 //     ranges is finished by a log-sum-exp merge of the pieces, in the
@@ -153,7 +153,7 @@ struct RawV {
 // Buffer loads over the (head, slot) ranges of the cache: keys past Tc fall
 // outside the K range and read as zero, value tokens past Tv are sent out of
 // range.  No branch, so the loads stay in flight until the codes are
-// dequantized two phases later.  lt is the thread's index in its group.
+// dequantized in the next phase.  lt is the thread's index in its group.
 // bf16 baseline format: the same elements as bf16 (two 16-byte words per
 // 16 elements).
 struct RawKB {
@@ -504,7 +504,7 @@ __device__ __forceinline__ void lds_barrier() {
 // are complete, and up to 8 of the reads stay in flight.  LDS operations of
 // a wave complete in order, so at most 8 outstanding means that everything
 // issued before the last 8 reads is done.  The reads' buffer is next written
-// three phases later.
+// at least three phases later.
 __device__ __forceinline__ void barrier_v_reads_in_flight() {
   asm volatile("s_waitcnt lgkmcnt(8)\n\ts_barrier" ::: "memory");
 }
