@@ -505,6 +505,7 @@ __device__ __forceinline__ void lds_barrier() {
 // a wave complete in order, so at most 8 outstanding means that everything
 // issued before the last 8 reads is done.  The reads' buffer is next written
 // at least three phases later.
+static_assert(128 / 8 >= 8 && 64 / 8 >= 8, "at least 8 V-operand reads follow the tile stores");
 __device__ __forceinline__ void barrier_v_reads_in_flight() {
   asm volatile("s_waitcnt lgkmcnt(8)\n\ts_barrier" ::: "memory");
 }
@@ -890,6 +891,9 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
           // The group's half of tile t + 2 (its codes were loaded in the MFMA
           // phase), then the V operands of tile t for the next MFMA phase
           dequant_tile();
+          // the tile stores stay ahead of the V reads (the barrier after this
+          // phase waits for all but the last 8 LDS operations)
+          asm volatile("" ::: "memory");
           if constexpr (L) read_v_operands<D>(va, sm.vt[t % kVBufs], n, hf);
         };
 
