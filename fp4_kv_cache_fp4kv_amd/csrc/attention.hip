@@ -134,8 +134,6 @@ struct Smem {
   int fl_shot[FP4KV_MAX_SLOTS];
   float fl_gk[FP4KV_MAX_SLOTS];
   float fl_gv[FP4KV_MAX_SLOTS];
-  int n_fl;
-  int seg_c0, seg_c1;   // walk range [seg_c0, seg_c1) of the current segment
   int merge_last;       // this workgroup completes the current row block
 };
 
@@ -519,6 +517,16 @@ __device__ __forceinline__ const AttnParams &opaque_params() {
   return *(const AttnParams *)kp;
 }
 
+// This lane's index within its wave, computed by an instruction the compiler
+// cannot move or merge (the count of the wave's lanes below this one), so
+// that a value derived from it is derived again where it is needed instead
+// of being held across a loop.
+__device__ __forceinline__ int fresh_lane() {
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  return lane;
+}
+
 // First virtual tile of workgroup w when n_units tiles are cut into n_wg
 // contiguous ranges of (nearly) equal length.
 __device__ __forceinline__ long long split_start(int w, long long n_units, int n_wg) {
@@ -571,13 +579,6 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   Smem<D> &sm = *reinterpret_cast<Smem<D> *>(smem_raw);
 
-  const int n_qt = (p.Nq + kBM - 1) / kBM;
-  const int n_tiles = (p.Tc + kBN - 1) / kBN;
-  const int last_nval = p.Tc - (n_tiles - 1) * kBN;
-  const int half_rot = p.rot_dim >> 1;
-  const int f1 = p.q_frame0 + p.n_q_frames;
-  const int ws = max(p.S, f1 - p.W);
-
   // ---- split schedule.  A row block (kBM query rows of one head, head-major
   // order) has n_v virtual tiles, n_tiles per cache slot; the n_wg
   // workgroups take equal contiguous ranges of the virtual tiles of all row
@@ -592,27 +593,44 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
   const int per = (int)gridDim.x / kXcds;
   const int w = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
   if (w >= p.n_wg) return;
-  const long long n_v = (long long)p.n_slots * n_tiles;
-  const long long n_units = (long long)n_qt * p.H * n_v;
+  const long long n_v = (long long)p.n_slots * ((p.Tc + kBN - 1) / kBN);
+  const long long n_units = (long long)((p.Nq + kBM - 1) / kBM) * p.H * n_v;
   const long long u0 = split_start(w, n_units, p.n_wg);
   const long long u1 = split_start(w + 1, n_units, p.n_wg);
   if (u0 >= u1) return;
-  const long long blk0 = u0 / n_v;
-  for (long long blk = blk0; blk * n_v < u1; ++blk) {
-    const long long vbase = blk * n_v;
-    const int v_lo = (int)(max(u0, vbase) - vbase), v_hi = (int)(min(u1, vbase + n_v) - vbase);
+  // The range covers row blocks blk0 .. blk0 + n_blk - 1, from virtual tile
+  // lo0 of the first to hi_last of the last.  Row block indices (below 2^23,
+  // as rows x heads < 2^31) and n_v (64 slots of < 2^18 tiles) fit in int,
+  // so the segment loop runs on 32-bit scalar arithmetic.
+  const int blk0 = (int)(u0 / n_v);
+  const int n_blk = (int)((u1 - 1) / n_v) - blk0 + 1;
+  const int lo0 = (int)(u0 - blk0 * n_v);
+  const int hi_last = (int)(u1 - (blk0 + n_blk - 1) * n_v);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  for (int bi = 0; bi < n_blk; ++bi) {
+    const int blk = blk0 + bi;
     // Every wave has finished reading the previous row block's frame list,
     // turn table and tiles once it passes this barrier.  (The first row
     // block needs none; the barrier is unconditional so that the protocol
     // does not depend on the order in which row blocks are visited.)
     __syncthreads();
-    // The kernel arguments and the thread index are made opaque in every
-    // segment, so that the compiler derives addresses and divisors here
-    // instead of holding them (spilled) across the segment loop.
+    // The kernel arguments and the lane index are made opaque in every
+    // segment (opaque_params, fresh_lane), so that the compiler derives
+    // addresses, divisors and thread indices here instead of holding them
+    // (spilled) across the segment loop.
     const AttnParams &p = opaque_params();
-    int tid = (int)threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    const int wave = tid >> 6, lane = tid & 63;
+    const int lane = fresh_lane();
+    const int tid = wave * 64 + lane;
+    const int n_qt = (p.Nq + kBM - 1) / kBM;
+    const int n_tiles = (p.Tc + kBN - 1) / kBN;
+    const int last_nval = p.Tc - (n_tiles - 1) * kBN;
+    const int half_rot = p.rot_dim >> 1;
+    const int f1 = p.q_frame0 + p.n_q_frames;
+    const int ws = max(p.S, f1 - p.W);
+    const int n_v = p.n_slots * n_tiles;
+    const long long n_units = (long long)n_qt * p.H * n_v;
+    const long long vbase = (long long)blk * n_v;
+    const int v_lo = bi == 0 ? lo0 : 0, v_hi = bi == n_blk - 1 ? hi_last : n_v;
     const int n = lane & 31, hf = lane >> 5;
     const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);
     const int lt = tid & 255;   // thread index within the group
@@ -624,50 +642,46 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     const int my_qshot = p.q_shot[my_qf - p.q_frame0];
     const int my_qchunk = my_qf / p.C;
 
-    // ---- visible key frames of this workgroup (one wave, ballot compaction)
-    if (wave == 0) {
-      const int qf_lo = p.q_frame0 + wg_row0 / p.T;
-      const int qf_hi = p.q_frame0 + (min(p.Nq, wg_row0 + kBM) - 1) / p.T;
-      bool ok = false;
-      int kf = -1, kshot = 0;
-      bool sink = false;
-      if (lane < p.n_slots) {
-        kf = p.slot_frame[lane];
-        kshot = p.slot_shot[lane];
-        // a sink slot holds frame kf < S of the stream (seen across shots),
-        // or with per-shot sinks one of the first S frames of some shot
-        // (seen by that shot only); its position is its slot
-        sink = p.sink_per_shot ? lane < p.S : kf < p.S;
-        const bool exempt = sink && !p.sink_per_shot;
-        ok = kf >= 0 && kf < f1 && (sink || kf >= ws);
-        if (ok) {
-          bool any = false;
-          for (int qf = qf_lo; qf <= qf_hi; ++qf)
-            any |= (kf / p.C <= qf / p.C) && (exempt || kshot == p.q_shot[qf - p.q_frame0]);
-          ok = any;
-        }
-      }
-      const unsigned long long mask = __ballot(ok);
-      const int idx = __popcll(mask & ((1ull << lane) - 1ull));
+    // ---- visible key frames of this row block (ballot over the slots).
+    // Every wave derives the mask, and from it the segment's walk range, in
+    // scalar registers; wave 0 writes the compacted frame list.
+    const int qf_lo = p.q_frame0 + wg_row0 / p.T;
+    const int qf_hi = p.q_frame0 + (min(p.Nq, wg_row0 + kBM) - 1) / p.T;
+    bool ok = false;
+    int kf = -1, kshot = 0;
+    bool sink = false;
+    if (lane < p.n_slots) {
+      kf = p.slot_frame[lane];
+      kshot = p.slot_shot[lane];
+      // a sink slot holds frame kf < S of the stream (seen across shots),
+      // or with per-shot sinks one of the first S frames of some shot
+      // (seen by that shot only); its position is its slot
+      sink = p.sink_per_shot ? lane < p.S : kf < p.S;
+      const bool exempt = sink && !p.sink_per_shot;
+      ok = kf >= 0 && kf < f1 && (sink || kf >= ws);
       if (ok) {
-        sm.fl_slot[idx] = lane;
-        sm.fl_kf[idx] = kf;
-        sm.fl_pos[idx] = sink ? lane : p.S + (kf - ws);
-        sm.fl_shot[idx] = kshot;
-        sm.fl_gk[idx] = p.k_tscale[lane];
-        sm.fl_gv[idx] = p.v_tscale[lane];
+        bool any = false;
+        for (int qf = qf_lo; qf <= qf_hi; ++qf)
+          any |= (kf / p.C <= qf / p.C) && (exempt || kshot == p.q_shot[qf - p.q_frame0]);
+        ok = any;
       }
-      if (lane == 0) {
-        sm.n_fl = __popcll(mask);
-        sm.seg_c0 = walk_index(mask, v_lo, n_tiles);
-        sm.seg_c1 = walk_index(mask, v_hi, n_tiles);
-      }
+    }
+    const unsigned long long mask = __ballot(ok);
+    if (wave == 0 && ok) {
+      const int idx = __popcll(mask & ((1ull << lane) - 1ull));
+      sm.fl_slot[idx] = lane;
+      sm.fl_kf[idx] = kf;
+      sm.fl_pos[idx] = sink ? lane : p.S + (kf - ws);
+      sm.fl_shot[idx] = kshot;
+      sm.fl_gk[idx] = p.k_tscale[lane];
+      sm.fl_gv[idx] = p.v_tscale[lane];
     }
     __syncthreads();
 
     // The segment walks the tiles [c0, c0 + n_total) of the row block's walk,
     // from tile ta of listed frame fa to tile te of listed frame fe.
-    const int c0 = sm.seg_c0, n_total = sm.seg_c1 - c0;
+    const int c0 = walk_index(mask, v_lo, n_tiles);
+    const int n_total = walk_index(mask, v_hi, n_tiles) - c0;
     const int fa = c0 / n_tiles, ta = c0 - fa * n_tiles;
     const int fe = (c0 + max(n_total, 1) - 1) / n_tiles, te = c0 + max(n_total, 1) - 1 - fe * n_tiles;
 
@@ -937,16 +951,21 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
       }
     }
 
-    // ---- epilogue: O = g_v * acc / l, g_v of the last frame walked
+    // ---- epilogue: O = g_v * acc / l, g_v of the last frame walked.  The
+    // lane's rows are derived again, so that nothing per lane is held across
+    // the tile loop.
+    const int e_lane = fresh_lane();
+    const int e_n = e_lane & 31, e_hf = e_lane >> 5;
+    const int e_row = wave * 32 + e_n, e_my_row = wg_row0 + e_row;
     const float l = halves_sum(lsum[0]);
     auto store_out = [&](float inv) __attribute__((always_inline)) {
-      if (!row_ok) return;
-      const long long obase = ((long long)my_row * p.H + head) * D;
+      if (e_my_row >= p.Nq) return;
+      const long long obase = ((long long)e_my_row * p.H + head) * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int d = 32 * db + 8 * i + 4 * hf;
+          const int d = 32 * db + 8 * i + 4 * e_hf;
           const float v0 = oacc[db][4 * i] * inv, v1 = oacc[db][4 * i + 1] * inv;
           const float v2 = oacc[db][4 * i + 2] * inv, v3 = oacc[db][4 * i + 3] * inv;
           if (OUT_F32) {
@@ -968,14 +987,13 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     // Pieces are written and read with device-coherent (sc1) accesses, which
     // do not stop in an XCD's L2, so no L2 writeback or invalidation is
     // needed between workgroups on different XCDs.
-    const int row = wave * 32 + n;
     const __amdgpu_buffer_rsrc_t ws_o =
         rsrc((const uint8_t *)p.ws_o, (uint32_t)(2 * p.n_wg * kBM * D * 4));
     const __amdgpu_buffer_rsrc_t ws_ml =
         rsrc((const uint8_t *)p.ws_ml, (uint32_t)(2 * p.n_wg * kBM * 8));
     {
-      const int slot = blk == blk0 ? 2 * w : 2 * w + 1;
-      const int ob = ((slot * kBM + row) * D + 4 * hf) * 4;
+      const int slot = bi == 0 ? 2 * w : 2 * w + 1;
+      const int ob = ((slot * kBM + e_row) * D + 4 * e_hf) * 4;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -988,9 +1006,9 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
           }
           __builtin_amdgcn_raw_buffer_store_b128(x, ws_o, ob + (32 * db + 8 * i) * 4, 0, kSc1);
         }
-      if (hf == 0) {
+      if (e_hf == 0) {
         const u32x2 ml = {__float_as_uint(m_run), __float_as_uint(l)};
-        __builtin_amdgcn_raw_buffer_store_b64(ml, ws_ml, (slot * kBM + row) * 8, 0, kSc1);
+        __builtin_amdgcn_raw_buffer_store_b64(ml, ws_ml, (slot * kBM + e_row) * 8, 0, kSc1);
       }
     }
     if (p.merge_pass) continue;   // merge_kernel combines the pieces
@@ -998,12 +1016,12 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     const int w_last = split_owner(vbase + n_v - 1, n_units, p.n_wg);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the piece is written
     __syncthreads();
-    if (tid == 0)
+    if (wave == 0 && e_lane == 0)
       sm.merge_last = __hip_atomic_fetch_add(p.ws_cnt + w_first, 1, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT) == w_last - w_first;
     __syncthreads();
     if (!sm.merge_last) continue;
-    if (tid == 0)   // ready for the next launch
+    if (wave == 0 && e_lane == 0)   // ready for the next launch
       __hip_atomic_store(p.ws_cnt + w_first, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // ---- the last piece in: log-sum-exp merge of all pieces of the row
@@ -1016,14 +1034,14 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
       for (int j = 0; j < 16; ++j) oacc[db][j] = 0.0f;
     for (int wc = w_first; wc <= w_last; ++wc) {
       const int slot = 2 * wc + (split_start(wc, n_units, p.n_wg) < vbase ? 1 : 0);
-      const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(ws_ml, (slot * kBM + row) * 8, 0, kSc1);
+      const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(ws_ml, (slot * kBM + e_row) * 8, 0, kSc1);
       const float m_in = __uint_as_float(ml[0]), l_in = __uint_as_float(ml[1]);
       const float m_new = fmaxf(m_all, m_in);
       const float a_old = __builtin_amdgcn_exp2f(m_all - m_new);
       const float a_in = __builtin_amdgcn_exp2f(m_in - m_new);
       m_all = m_new;
       l_all = merge_step(l_all, a_old, l_in, a_in);
-      const int ib = ((slot * kBM + row) * D + 4 * hf) * 4;
+      const int ib = ((slot * kBM + e_row) * D + 4 * e_hf) * 4;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll

@@ -75,9 +75,9 @@ def segment_events(n_total, frames, lists, merge, live, kbufs, vbufs):
     for wave in range(8):
         G, L = wave >> 2, live[wave]
         ev = [('B',)]
-        if wave == 0:                                   # frame list, segment bounds
-            ev += [('W', loc, 0) for loc in lists] + [('W', 'seg', 0)]
-        ev += [('B',), ('R', 'seg', 0)]
+        if wave == 0:                                   # frame list (every wave
+            ev += [('W', loc, 0) for loc in lists]      # derives the walk range)
+        ev += [('B',)]
         if n_total == 0:
             if merge:
                 ev += [('B',)] + ([('W', 'merge', 0)] if wave == 0 else []) + [('B',), ('R', 'merge', 0)]
