@@ -199,11 +199,26 @@ __device__ __forceinline__ SlotRes slot_resources(const AttnParams &p, int head,
   return r;
 }
 
+// K-tile work of group thread lt: key within the tile and 32-dimension part.
+// At D = 128 the 8 lanes that store together take 4 keys x 2 parts, so their
+// 16-byte stores fall on 8 different groups of 4 LDS banks (stores are
+// served 8 lanes at a time); each wave still loads 16 whole keys.
+template <int D>
+__device__ __forceinline__ int k_key(int lt) {
+  if constexpr (D == 128) return (lt & 3) | ((lt >> 1) & 12) | ((lt >> 6) << 4);
+  return lt / (D / 32);
+}
+template <int D>
+__device__ __forceinline__ int k_part(int lt) {
+  if constexpr (D == 128) return ((lt >> 2) & 1) | ((lt >> 4) & 2);
+  return lt % (D / 32);
+}
+
 template <int D>
 __device__ __forceinline__ void load_k(const SlotRes &sr, int k0, int lt, RawK &r) {
   constexpr int KU = D / 32;
   if (lt < kBN * KU) {   // every thread of the group for D = 128
-    const uint32_t key = k0 + lt / KU, qd = lt % KU;
+    const uint32_t key = k0 + k_key<D>(lt), qd = k_part<D>(lt);
     const auto kc = __builtin_amdgcn_raw_buffer_load_b128(sr.kc, key * (D / 2) + 16 * qd, 0, 0);
     r.kc = make_uint4(kc[0], kc[1], kc[2], kc[3]);
     r.ks = __builtin_amdgcn_raw_buffer_load_b16(sr.ks, key * (D / 16) + 2 * qd, 0, 0);
@@ -231,7 +246,7 @@ template <int D>
 __device__ __forceinline__ void load_k(const SlotRes &sr, int k0, int lt, RawKB &r) {
   constexpr int KU = D / 32;
   if (lt < kBN * KU) {
-    const uint32_t off = (k0 + lt / KU) * (D * 2) + 64 * (lt % KU);
+    const uint32_t off = (k0 + k_key<D>(lt)) * (D * 2) + 64 * k_part<D>(lt);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const auto w = __builtin_amdgcn_raw_buffer_load_b128(sr.kc, off + 16 * i, 0, 0);
@@ -277,7 +292,7 @@ template <int D>
 __device__ __forceinline__ void dequant_k(const RawK &r, int lt, uint16_t (*kt)[D + kPad]) {
   constexpr int KU = D / 32;
   if (lt < kBN * KU) {
-    const int key = lt / KU, qd = lt % KU;
+    const int key = k_key<D>(lt), qd = k_part<D>(lt);
     const f16x2 s2 = fp8x2<false>(r.ks);
     const f16x2 sa = {s2[0], s2[0]}, sb = {s2[1], s2[1]};
     const uint32_t cw[4] = {r.kc.x, r.kc.y, r.kc.z, r.kc.w};
@@ -319,7 +334,7 @@ template <int D>
 __device__ __forceinline__ void dequant_k(const RawKB &r, int lt, uint16_t (*kt)[D + kPad]) {
   constexpr int KU = D / 32;
   if (lt < kBN * KU) {
-    const int key = lt / KU, qd = lt % KU;
+    const int key = k_key<D>(lt), qd = k_part<D>(lt);
     uint4 *dst = (uint4 *)&kt[krow_phys(key)][32 * qd];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
