@@ -332,16 +332,23 @@ __device__ __forceinline__ void rerot_encode(const AppendParams &p, int rb, uint
 
 // The step's first kernel when queries are rotated and a chunk appended in
 // one call: workgroups [0, 2 kAmaxBlocks) take the partial maxima of K and V
-// (as amax_kernel), the rest rotate the queries (as rope_kernel).  The
-// encode kernel follows on the same stream.
-__global__ __launch_bounds__(kThreads) void rope_amax_kernel(RopeParams rp, AppendParams ap) {
+// (as amax_kernel), the rest rotate the queries' units [0, n) (as
+// rope_kernel).  encode_rope_kernel follows on the same stream with the
+// remaining units.  The value encode is a few long-running workgroups (each
+// thread encodes 8 blocks), so the second kernel has idle CUs that part of
+// the rotation fills: with 5 of 8 eighths of the rotation in the first
+// kernel, the 1.3B-like step's append and rotation took 26.1 us cold instead
+// of 27.9 us with all of it there, and the 5B-like step's 27.5 instead of
+// 29.0 us.
+constexpr int kRopeFirstEighths = 5;
+__global__ __launch_bounds__(kThreads) void rope_amax_kernel(RopeParams rp, AppendParams ap,
+                                                             long long n) {
   __shared__ uint32_t red[kThreads / 64];
   const int b = (int)blockIdx.x;
   if (b < 2 * kAmaxBlocks) {
     amax_part(ap, b / kAmaxBlocks, b % kAmaxBlocks, kAmaxBlocks, red);
     return;
   }
-  const long long n = rope_units(rp);
   const long long nb = (long long)gridDim.x - 2 * kAmaxBlocks;
   for (long long u = (long long)(b - 2 * kAmaxBlocks) * kThreads + threadIdx.x; u < n;
        u += nb * kThreads)
@@ -356,19 +363,18 @@ __global__ __launch_bounds__(kThreads) void rope_amax_kernel(RopeParams rp, Appe
 // workgroups encode the keys, token-major: one thread per (token, 16-block),
 // blocks fastest, so a wave reads whole rows and writes contiguous bytes.
 // Workgroups past both re-encode the window slots a window move turns.
-__global__ __launch_bounds__(kThreads) void encode_kernel(AppendParams p) {
+__device__ __forceinline__ void encode_wg(const AppendParams &p, int bid, uint32_t *red) {
   const int nb = p.D >> 4;                                   // blocks per row
-  __shared__ uint32_t red[kThreads / 64];
-  if ((int)blockIdx.x >= p.v_blocks + p.k_blocks) {
-    rerot_encode(p, (int)blockIdx.x - p.v_blocks - p.k_blocks, red);
+  if (bid >= p.v_blocks + p.k_blocks) {
+    rerot_encode(p, bid - p.v_blocks - p.k_blocks, red);
     return;
   }
-  const bool is_v = (int)blockIdx.x < p.v_blocks;
+  const bool is_v = bid < p.v_blocks;
   const int y = is_v ? 1 : 0;
   const float g = p.tscale_in ? caller_scale(p.tscale_in[y]) : tensor_scale(p, y, red);
   const float d = 6.0f * g;
 
-  if ((blockIdx.x == 0 || (int)blockIdx.x == p.v_blocks) && threadIdx.x < p.n_frames) {
+  if ((bid == 0 || bid == p.v_blocks) && (int)threadIdx.x < p.n_frames) {
     const int j = threadIdx.x, f = p.frame0 + j;
     const int slot = slot_of(p, j);
     p.tscale[y][slot] = g;
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(AppendParams p) {
 
   if (!is_v) {
     const uint32_t units = (uint32_t)(p.H * p.n_frames * p.Tc * nb);
-    const uint32_t u = (blockIdx.x - p.v_blocks) * kThreads + threadIdx.x;
+    const uint32_t u = (uint32_t)(bid - p.v_blocks) * kThreads + threadIdx.x;
     if (u >= units) return;
     const int b = (int)(u % nb);
     uint32_t rest = u / nb;
@@ -401,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(AppendParams p) {
 
   const int groups = p.Tv >> 3;                              // 8-token groups
   const uint32_t units = (uint32_t)(p.H * p.n_frames * groups * nb);
-  const uint32_t u = blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t u = (uint32_t)bid * kThreads + threadIdx.x;
   if (u >= units) return;
   const int b = (int)(u % nb);
   uint32_t rest = u / nb;
@@ -438,6 +444,28 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(AppendParams p) {
     *(uint32_t *)(p.codes[1] + (vrow0 + r) * (p.Tv >> 1) + 4 * grp) = rows[r];
   const long long srow = ((long long)h * p.n_slots + slot) * nb + b;
   *(uint2 *)(p.scales[1] + srow * p.Tv + 8 * grp) = make_uint2(sc_lo, sc_hi);
+}
+__global__ __launch_bounds__(kThreads) void encode_kernel(AppendParams p) {
+  __shared__ uint32_t red[kThreads / 64];
+  encode_wg(p, (int)blockIdx.x, red);
+}
+
+// The step's second kernel: the encode (workgroups [0, v_blocks + k_blocks))
+// and, in the workgroups after it, the query rotation's units [u0, n), which
+// fill the CUs that the few long-running value workgroups leave idle.
+__global__ __launch_bounds__(kThreads) void encode_rope_kernel(AppendParams p, RopeParams rp,
+                                                               long long u0) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int enc = p.v_blocks + p.k_blocks;
+  if ((int)blockIdx.x < enc) {
+    encode_wg(p, (int)blockIdx.x, red);
+    return;
+  }
+  const long long n = rope_units(rp);
+  const long long nb = (long long)gridDim.x - enc;
+  for (long long u = u0 + (long long)((int)blockIdx.x - enc) * kThreads + threadIdx.x; u < n;
+       u += nb * kThreads)
+    rope_unit(rp, u);
 }
 
 // ---- bf16 baseline format: the append stores bf16, no quantization ----
@@ -627,14 +655,19 @@ hipError_t launch_rope_append(const RopeParams &rp, const AppendParams &ap_in, h
   append_blocks(ap);
   ap.amax_tensors = 2;
   const long long n = rope_units(rp);
-  long long rope_blocks = (n + kThreads - 1) / kThreads;
-  if (rope_blocks > 8192) rope_blocks = 8192;
-  if (rope_blocks < 1) rope_blocks = 1;
-  hipLaunchKernelGGL(rope_amax_kernel, dim3((unsigned)(2 * kAmaxBlocks + rope_blocks)),
-                     dim3(kThreads), 0, s, rp, ap);
-  const hipError_t e = hipGetLastError();
+  const long long n1 = n * kRopeFirstEighths / 8;   // units rotated in the first kernel
+  auto blocks_for = [](long long units) {
+    long long b = (units + kThreads - 1) / kThreads;
+    return b > 8192 ? 8192 : b;
+  };
+  hipLaunchKernelGGL(rope_amax_kernel, dim3((unsigned)(2 * kAmaxBlocks + blocks_for(n1))),
+                     dim3(kThreads), 0, s, rp, ap, n1);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_encode(ap, s);
+  const long long enc = (long long)ap.v_blocks + ap.k_blocks;
+  hipLaunchKernelGGL(encode_rope_kernel, dim3((unsigned)(enc + blocks_for(n - n1))),
+                     dim3(kThreads), 0, s, ap, rp, n1);
+  return hipGetLastError();
 }
 
 }  // namespace fp4kv
