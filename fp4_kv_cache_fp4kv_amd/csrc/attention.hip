@@ -614,9 +614,10 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
   const long long u1 = split_start(w + 1, n_units, p.n_wg);
   if (u0 >= u1) return;
   // The range covers row blocks blk0 .. blk0 + n_blk - 1, from virtual tile
-  // lo0 of the first to hi_last of the last.  Row block indices (below 2^23,
-  // as rows x heads < 2^31) and n_v (64 slots of < 2^18 tiles) fit in int,
-  // so the segment loop runs on 32-bit scalar arithmetic.
+  // lo0 of the first to hi_last of the last.  Row block indices (at most
+  // rows x heads / 256 + heads, with rows x heads <= 2^31) and n_v (64 slots
+  // of < 2^18 tiles) fit in int, so the segment loop runs on 32-bit scalar
+  // arithmetic; only u0, u1 and n_units need 64 bits.
   const int blk0 = (int)(u0 / n_v);
   const int n_blk = (int)((u1 - 1) / n_v) - blk0 + 1;
   const int lo0 = (int)(u0 - blk0 * n_v);
