@@ -513,14 +513,20 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Barrier at the end of a VALU phase of a wave that read V operands: its LDS
-// writes (the dequantized tile, issued before its D/8 >= 8 V-operand reads)
-// are complete, and up to 8 of the reads stay in flight.  LDS operations of
-// a wave complete in order, so at most 8 outstanding means that everything
-// issued before the last 8 reads is done.  The reads' buffer is next written
-// at least three phases later.
-static_assert(128 / 8 >= 8 && 64 / 8 >= 8, "at least 8 V-operand reads follow the tile stores");
+// writes (the dequantized tile, issued before its D/8 V-operand reads) are
+// complete, and up to min(D/8, 15) of the reads stay in flight (15 is the
+// largest count the wait takes).  LDS operations of a wave complete in
+// order, so at most N outstanding, N no larger than the reads that follow
+// the writes, means that every write is done; scalar loads that share the
+// counter only add to the operations already complete.  The reads' buffer is
+// next written at least three phases later.
+template <int D>
 __device__ __forceinline__ void barrier_v_reads_in_flight() {
-  asm volatile("s_waitcnt lgkmcnt(8)\n\ts_barrier" ::: "memory");
+  static_assert(D == 128 || D == 64, "V-operand reads per thread: D / 8");
+  if constexpr (D == 128)
+    asm volatile("s_waitcnt lgkmcnt(15)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt lgkmcnt(8)\n\ts_barrier" ::: "memory");
 }
 
 // The kernel's argument block (a single AttnParams at offset 0), read
@@ -942,7 +948,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
 
         if (G) lds_barrier();   // group 1's opening phase
         auto valu_barrier = [&]() __attribute__((always_inline)) {
-          if constexpr (L) barrier_v_reads_in_flight();
+          if constexpr (L) barrier_v_reads_in_flight<D>();
           else lds_barrier();   // no V reads follow the LDS writes
         };
         mfma_phase(0, BoolC<false>(), BoolC<true>());
