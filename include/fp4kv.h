@@ -371,11 +371,11 @@ int fp4kv_rope_rel_frames(const fp4kv_cache *c, const void *x, int in_dtype, voi
  * fp4kv_rope_append - the two codec steps of one chunk in one call and two
  * kernels: the rotation of the chunk's queries (fp4kv_rope_rel_frames of q
  * into q_rot) and the append of its keys and values
- * (fp4kv_quantize_append with tscale_in = NULL).  The first kernel rotates
- * the queries and takes the partial maxima of K and V, the second encodes K
- * and V into the cache ("fused RoPE" and "in-place quantized KV-cache
- * updates", hysenlabs.com, section "NVFP4, sequence parallel and the async
- * decode path").  Results are bit for bit those of the two separate calls.
+ * (fp4kv_quantize_append with tscale_in = NULL).  The first kernel takes the
+ * partial maxima of K and V and rotates part of the queries, the second
+ * encodes K and V into the cache and rotates the rest of the queries
+ * ("fused RoPE" and "in-place quantized KV-cache updates", hysenlabs.com,
+ * section "NVFP4, sequence parallel and the async decode path").  Results are bit for bit those of the two separate calls.
  * Arguments as in those calls; the cache must have format
  * FP4KV_FORMAT_NVFP4_V1 (FP4KV_EINVAL otherwise).  q_rot must not be k or v
  * (q_rot may be q when the dtypes match).
