@@ -484,13 +484,14 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic},
         # the step's codec kernels as timed inside the steps: for the NVFP4
-        # path the queries' rotation fused with the append (rope_amax_kernel,
-        # encode_rope_kernel); bytes = queries read and written as float32, kept
-        # K and V read once, codes and scales written once
+        # path the queries' rotation fused with the append (one pass,
+        # prologue_kernel, for the bf16 inputs here); bytes = queries read and
+        # written as float32, kept K and V read once, codes and scales written
+        # once
         "roofline_codec": {"bound": "hbm", "achieved": round(update_gbs, 1), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(update_gbs / HBM_PEAK_GBS, 4),
                            "bytes": int(m["update_bytes"]),
-                           "kernels": {"nvfp4": "rope_amax_kernel + encode_rope_kernel",
+                           "kernels": {"nvfp4": "prologue_kernel (one pass, bf16 inputs)",
                                        "nvfp4_rot": "amax_kernel + encode_kernel + rope_kernel",
                                        "bf16": "store_bf16_kernel + rope_kernel"}[args.kv]},
     }

@@ -14,7 +14,7 @@ using namespace fp4kv;
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -74,6 +74,7 @@ int from_hip(hipError_t e) { return e == hipSuccess ? FP4KV_OK : FP4KV_EDEVICE; 
 // Workspace fields of the codec's parameters.
 void set_append_ws(AppendParams &p, void *workspace) {
   p.ws_partial = (uint32_t *)workspace;
+  p.ws_bar = (uint32_t *)workspace + kWsBarOffset;
   p.ws_rr = (uint32_t *)workspace + kWsRrOffset;
   p.ws_rr_g = (float *)((uint32_t *)workspace + kWsRrGOffset);
 }

@@ -468,6 +468,248 @@ __global__ __launch_bounds__(kThreads) void encode_rope_kernel(AppendParams p, R
     rope_unit(rp, u);
 }
 
+// ---- the step's prologue in one pass (bf16 inputs) ----
+// One launch over a grid that is resident all at once (four workgroups per
+// CU, sized on the host from the kernel's occupancy):
+//   1. every thread loads one item, 4 kept tokens x one 16-element block of
+//      K or of V (128 bytes), and keeps it in registers; the workgroup's
+//      partial maxima of K and V go to the workspace;
+//   2. the workgroup arrives at a grid barrier, then rotates its share of
+//      the queries while the others arrive;
+//   3. once every workgroup has arrived, each folds the partial maxima into
+//      g = amax / 2688 per tensor and every thread encodes the item it
+//      holds.  The two threads of adjacent lanes hold the two 4-token halves
+//      of one 8-token value group and exchange their 16-bit halves of the
+//      group's code words.
+// K and V are read from memory once, against twice for the two-kernel form.
+// Cross-workgroup words (partial maxima, barrier counts and phases) are
+// written and read with device-coherent accesses that do not stop in an
+// XCD's L2, and a store is complete (vmcnt(0)) before the arrival that
+// publishes it.  Atomics on one address are served one at a time, so the
+// barrier has two levels: workgroup w counts in at group w % kBarGroups,
+// the last of each group at the top count, and the last of those flips
+// every group's phase word, which only that group's workgroups poll.  Each
+// count is cleared by its last arrival, so the workspace is left as found;
+// it must hold zeros before its first use.  A wait that exceeds
+// kBarrierSpins polls gives up: the workgroup sets the error word and skips
+// its encode instead of hanging.
+constexpr int kBarrierSpins = 1 << 20;
+constexpr int kSc1 = 16;   // cache-policy operand: sc1, a device-coherent access
+constexpr uint32_t kBufferWord3 = 0x00020000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(uint32_t *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, (int)kBufferWord3);
+}
+
+__device__ __forceinline__ void block_max2_u32(uint32_t &a, uint32_t &b, uint32_t (*red)[kThreads / 64]) {
+  a = wave_max_u32(a);
+  b = wave_max_u32(b);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    red[0][wave] = a;
+    red[1][wave] = b;
+  }
+  __syncthreads();
+  a = red[0][0];
+  b = red[1][0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) {
+    a = a > red[0][w] ? a : red[0][w];
+    b = b > red[1][w] ? b : red[1][w];
+  }
+  __syncthreads();   // red is reused
+}
+
+// Items of the one-pass prologue: K items first, then V items; each is
+// (head h, frame j, 4-token quarter-group qg, block b) with the two halves
+// of an 8-token group in adjacent lanes and b next, so 16 lanes read a
+// whole (token, head) row per token.  V items cover the padded tokens up to
+// Tv (a multiple of 8); K items stop at the last kept token's 8-token group.
+__host__ __device__ inline long long prologue_k_items(const AppendParams &p) {
+  return (long long)p.H * p.n_frames * ((p.Tc + 7) >> 3) * (p.D >> 4) * 2;
+}
+__host__ __device__ inline long long prologue_v_items(const AppendParams &p) {
+  return (long long)p.H * p.n_frames * (p.Tv >> 3) * (p.D >> 4) * 2;
+}
+
+__global__ __launch_bounds__(kThreads, 4) void prologue_kernel(RopeParams rp, AppendParams p) {
+  __shared__ uint32_t red[2][kThreads / 64];
+  __shared__ int go;
+  const int G = (int)gridDim.x;
+  const int nb = p.D >> 4;
+  const uint32_t k_items = (uint32_t)prologue_k_items(p);
+  const uint32_t n_items = k_items + (uint32_t)prologue_v_items(p);
+  const uint32_t u = blockIdx.x * kThreads + threadIdx.x;
+  // K items and V items are even in number, so both threads of a lane pair
+  // hold items of the same tensor, group and block
+  const bool has = u < n_items;
+  const bool is_v = u >= k_items;
+  const uint32_t iu = is_v ? u - k_items : u;
+  const int groups = is_v ? (p.Tv >> 3) : ((p.Tc + 7) >> 3);
+  const int half = (int)(iu & 1u);
+  uint32_t rest = iu >> 1;
+  const int b = (int)(rest % nb);
+  rest /= nb;
+  const int grp = (int)(rest % groups);
+  rest /= groups;
+  const int j = (int)(rest % p.n_frames);
+  const int h = (int)(rest / p.n_frames);
+  const int tc0 = 8 * grp + 4 * half;   // first of the item's 4 tokens
+
+  // ---- 1. the item, 4 tokens of one block, held until the encode
+  uint4 w[8];
+  {
+    const uint16_t *src = (const uint16_t *)p.x[is_v ? 1 : 0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tc = tc0 + i;
+      if (has && tc < p.Tc) {
+        const long long tok = (long long)j * p.T + (long long)tc * p.stride;
+        const uint4 *q = (const uint4 *)(src + (tok * p.H + h) * p.D + b * 16);
+        w[2 * i] = q[0];
+        w[2 * i + 1] = q[1];
+      } else {
+        w[2 * i] = make_uint4(0, 0, 0, 0);
+        w[2 * i + 1] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fold_max(m, w[i], true);
+  m = max(m & 0xFFFFu, m >> 16) << 16;   // bf16 bits -> float32 bits
+  uint32_t mk = (has && !is_v) ? m : 0u, mv = (has && is_v) ? m : 0u;
+  block_max2_u32(mk, mv, red);
+
+  // ---- 2. publish the partial maxima, arrive, rotate the queries' share
+  const __amdgpu_buffer_rsrc_t part = ws_rsrc(p.ws_rr, (uint32_t)(2 * G * 4));
+  const int n_groups = G < kBarGroups ? G : kBarGroups;
+  const int grp_of_wg = (int)blockIdx.x % n_groups;
+  const uint32_t grp_size = (uint32_t)((G - grp_of_wg + n_groups - 1) / n_groups);
+  uint32_t *cnt = p.ws_bar + grp_of_wg * kBarLine, *phase = cnt + kWsBarPhase;
+  uint32_t *top = p.ws_bar + kWsBarTop, *err = p.ws_bar + kWsBarError;
+  uint32_t phase0 = 0;
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_raw_buffer_store_b32(mk, part, 4 * (int)blockIdx.x, 0, kSc1);
+    __builtin_amdgcn_raw_buffer_store_b32(mv, part, 4 * (G + (int)blockIdx.x), 0, kSc1);
+    phase0 = __hip_atomic_load(phase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the maxima are stored and the phase is read before the arrival counts
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == grp_size - 1u) {   // the group is complete: reset, count it in
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t old_top =
+          __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old_top == (uint32_t)n_groups - 1u) {   // every group: reset, release all
+        __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        for (int g2 = 0; g2 < n_groups; ++g2)
+          __hip_atomic_store(p.ws_bar + g2 * kBarLine + kWsBarPhase, phase0 ^ 1u,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  {
+    // four units' reads in flight per thread
+    const long long n = rope_units(rp), step = (long long)G * kThreads;
+    for (long long q = u; q < n; q += 4 * step) {
+      RopeIn in[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (q + k * step < n) in[k] = rope_load(rp, q + k * step);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (q + k * step < n) rope_finish(rp, q + k * step, in[k]);
+    }
+  }
+
+  // ---- 3. wait for every arrival, fold the maxima, encode the item
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    for (int it = 0; __hip_atomic_load(phase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == phase0;
+         ++it) {
+      if (it >= kBarrierSpins) {
+        __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    go = ok;
+  }
+  __syncthreads();
+  if (!go) return;
+  uint32_t ak = 0u, av = 0u;
+  for (int i = threadIdx.x; i < G; i += kThreads) {
+    ak = max(ak, __builtin_amdgcn_raw_buffer_load_b32(part, 4 * i, 0, kSc1));
+    av = max(av, __builtin_amdgcn_raw_buffer_load_b32(part, 4 * (G + i), 0, kSc1));
+  }
+  block_max2_u32(ak, av, red);
+  const float amax_k = __uint_as_float(ak), amax_v = __uint_as_float(av);
+  const float gk = amax_k > 0.0f ? __fdiv_rn(amax_k, 2688.0f) : 1.0f;
+  const float gv = amax_v > 0.0f ? __fdiv_rn(amax_v, 2688.0f) : 1.0f;
+  if (blockIdx.x == 0 && (int)threadIdx.x < p.n_frames) {
+    const int jj = threadIdx.x, slot = slot_of(p, jj);
+    p.tscale[0][slot] = gk;
+    p.tscale[1][slot] = gv;
+    p.slot_frame[slot] = p.frame0 + jj;
+    p.slot_shot[slot] = p.shot[jj];
+  }
+  const float g = is_v ? gv : gk;
+  const float d = 6.0f * g;
+  const int slot = has ? slot_of(p, j) : 0;
+  uint32_t rows[16];   // values: 4 token nibbles (16 bits) per dimension
+#pragma unroll
+  for (int r = 0; r < 16; ++r) rows[r] = 0u;
+  uint32_t sc = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tc = tc0 + i;
+    if (!has || tc >= p.Tc) continue;   // past the frame: no key; value padding stays zero
+    const uint32_t ww[8] = {w[2 * i].x, w[2 * i].y, w[2 * i].z, w[2 * i].w,
+                            w[2 * i + 1].x, w[2 * i + 1].y, w[2 * i + 1].z, w[2 * i + 1].w};
+    float x[16];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[2 * e] = __uint_as_float(ww[e] << 16);
+      x[2 * e + 1] = __uint_as_float(ww[e] & 0xFFFF0000u);
+    }
+    uint32_t s8;
+    const uint2 packed = encode_block(x, g, d, &s8);
+    if (!is_v) {
+      const long long row = ((long long)h * p.n_slots + slot) * p.Tc + tc;
+      *(uint2 *)(p.codes[0] + row * (p.D >> 1) + b * 8) = packed;
+      p.scales[0][row * nb + b] = (uint8_t)s8;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t code = ((r < 8 ? packed.x : packed.y) >> (4 * (r & 7))) & 0xFu;
+        rows[r] |= code << (4 * i);
+      }
+      sc |= s8 << (8 * i);
+    }
+  }
+  // Value word of dimension r of the group: the even lane's 4 tokens in the
+  // low 16 bits, the odd lane's in the high 16 bits.  The even lane writes
+  // dimensions 0-7 and the odd lane 8-15, each taking the other's half by
+  // one exchange per word.  Every lane takes part (shuffles need them all).
+  uint32_t word[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const uint32_t give = half ? rows[r] : rows[r + 8];
+    const uint32_t got = (uint32_t)__shfl_xor((int)give, 1, 64);
+    word[r] = half ? (got | (rows[r + 8] << 16)) : (rows[r] | (got << 16));
+  }
+  if (has && is_v) {
+    const long long vrow0 = ((long long)h * p.n_slots + slot) * p.D + 16 * b + 8 * half;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      *(uint32_t *)(p.codes[1] + (vrow0 + r) * (p.Tv >> 1) + 4 * grp) = word[r];
+    const long long srow = ((long long)h * p.n_slots + slot) * nb + b;
+    *(uint32_t *)(p.scales[1] + srow * p.Tv + tc0) = sc;
+  }
+}
+
 // ---- bf16 baseline format: the append stores bf16, no quantization ----
 
 // float32 -> bf16 bits, round to nearest even (finite inputs)
@@ -650,10 +892,52 @@ hipError_t launch_append(const AppendParams &p_in, hipStream_t s) {
   return launch_encode(p, s);
 }
 
+namespace {
+// Workgroups of prologue_kernel that one device holds at once: compute
+// units x resident workgroups per unit (resolved once per device).
+std::mutex g_resident_mu;
+int g_resident[kMaxDevices];
+
+hipError_t prologue_resident(int *out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_resident_mu);
+  if (!g_resident[dev]) {
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prologue_kernel, kThreads, 0);
+    if (e != hipSuccess) return e;
+    g_resident[dev] = cus * (per_cu < 0 ? 0 : per_cu);
+    if (!g_resident[dev]) g_resident[dev] = -1;
+  }
+  *out = g_resident[dev];
+  return hipSuccess;
+}
+}  // namespace
+
 hipError_t launch_rope_append(const RopeParams &rp, const AppendParams &ap_in, hipStream_t s) {
   AppendParams ap = ap_in;   // NVFP4 cache, computed tensor scales, no window move
   append_blocks(ap);
   ap.amax_tensors = 2;
+  if (ap.in_bf16) {
+    // One pass when every item has a thread in a grid that the device
+    // holds at once; the grid is all that fits, so the rotation's reads in
+    // flight fill every compute unit (workgroups past the items rotate
+    // only).
+    int resident = 0;
+    hipError_t e = prologue_resident(&resident);
+    if (e != hipSuccess) return e;
+    const long long items = prologue_k_items(ap) + prologue_v_items(ap);
+    const long long need = (items + kThreads - 1) / kThreads;
+    const long long grid = resident < kPrologueMaxGrid ? resident : kPrologueMaxGrid;
+    if (resident > 0 && need <= grid) {
+      hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, rp, ap);
+      return hipGetLastError();
+    }
+  }
   const long long n = rope_units(rp);
   const long long n1 = n * kRopeFirstEighths / 8;   // units rotated in the first kernel
   auto blocks_for = [](long long units) {

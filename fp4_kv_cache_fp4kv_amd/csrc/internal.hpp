@@ -16,9 +16,23 @@ constexpr int kAmaxBlocks = 256;
 // appended K and V [2][kAmaxBlocks], then of each re-encoded window slot
 // [FP4KV_MAX_SLOTS][kAmaxBlocks], then the slots' previous key tensor scales
 // [FP4KV_MAX_SLOTS] (float32).
+// The one-pass step prologue keeps its partial maxima [2][grid] in the
+// re-encoding region and its grid barrier in the last 8448 bytes: for each
+// of kBarGroups groups of workgroups a 256-byte line with the group's
+// arrival count (word 0) and the phase its workgroups watch (word 32), then
+// a line with the count of groups complete (word 0) and a sticky error word
+// (word 32) set when a wait gave up.  The barrier words must be zero before
+// the first use and every call leaves the counts at zero.
 constexpr size_t kWsRrOffset = 2 * kAmaxBlocks;                        // in uint32
 constexpr size_t kWsRrGOffset = kWsRrOffset + (size_t)FP4KV_MAX_SLOTS * kAmaxBlocks;
-constexpr size_t kWsBytes = (kWsRrGOffset + FP4KV_MAX_SLOTS) * sizeof(uint32_t);
+constexpr size_t kWsBarOffset = (kWsRrGOffset + FP4KV_MAX_SLOTS + 63) / 64 * 64;
+constexpr int kBarGroups = 32, kBarLine = 64;   // a line is 64 words
+constexpr int kWsBarPhase = 32, kWsBarWords = (kBarGroups + 1) * kBarLine;
+constexpr int kWsBarTop = kBarGroups * kBarLine, kWsBarError = kWsBarTop + 32;
+constexpr size_t kWsBytes = (kWsBarOffset + kWsBarWords) * sizeof(uint32_t);
+// Largest grid of the one-pass prologue: its partial maxima fill the
+// re-encoding region.
+constexpr int kPrologueMaxGrid = (int)(FP4KV_MAX_SLOTS * kAmaxBlocks / 2);
 
 struct AppendParams {
   const void *x[2];        // K, V inputs [n_frames*T][H][D]
@@ -28,6 +42,7 @@ struct AppendParams {
   int32_t *slot_frame, *slot_shot;
   const float *tscale_in;  // device [2] or null
   uint32_t *ws_partial;    // [2][kAmaxBlocks]
+  uint32_t *ws_bar;        // grid barrier words of the one-pass prologue
   int H, D, T, stride, Tc, Tv, S, W, n_slots, frame0, n_frames;
   int in_bf16;
   int bf16_cache;          // FP4KV_FORMAT_BF16_V1: store bf16, no quantization

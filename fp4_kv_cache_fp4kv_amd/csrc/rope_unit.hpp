@@ -11,7 +11,25 @@
 
 namespace fp4kv {
 
-__device__ __forceinline__ void rope_unit(const RopeParams &p, long long u) {
+// The unit's 8 input elements (one 16- or 32-byte read).
+struct RopeIn {
+  uint4 a, b;   // b is used by float32 inputs only
+};
+__device__ __forceinline__ RopeIn rope_load(const RopeParams &p, long long u) {
+  const long long off = u * 8;   // units are consecutive 8-element groups
+  RopeIn in;
+  if (p.in_bf16) {
+    in.a = *(const uint4 *)((const uint16_t *)p.x + off);
+    in.b = make_uint4(0, 0, 0, 0);
+  } else {
+    in.a = *(const uint4 *)((const float *)p.x + off);
+    in.b = *(const uint4 *)((const float *)p.x + off + 4);
+  }
+  return in;
+}
+
+// Rotates unit u from its loaded elements and stores it.
+__device__ __forceinline__ void rope_finish(const RopeParams &p, long long u, const RopeIn &in) {
   const int groups = p.D >> 3;
   const int half = p.rot_dim >> 1;
   const int gi = (int)(u % groups);
@@ -22,18 +40,17 @@ __device__ __forceinline__ void rope_unit(const RopeParams &p, long long u) {
   const long long off = row * p.D + gi * 8;
   float x[8];
   if (p.in_bf16) {
-    const uint4 v = *(const uint4 *)((const uint16_t *)p.x + off);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t w[4] = {in.a.x, in.a.y, in.a.z, in.a.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[2 * i] = __uint_as_float(w[i] << 16);
       x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   } else {
-    const float4 a = *(const float4 *)((const float *)p.x + off);
-    const float4 b = *(const float4 *)((const float *)p.x + off + 4);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    x[0] = __uint_as_float(in.a.x); x[1] = __uint_as_float(in.a.y);
+    x[2] = __uint_as_float(in.a.z); x[3] = __uint_as_float(in.a.w);
+    x[4] = __uint_as_float(in.b.x); x[5] = __uint_as_float(in.b.y);
+    x[6] = __uint_as_float(in.b.z); x[7] = __uint_as_float(in.b.w);
   }
   const float *tab = p.cos_sin + (long long)pos * p.rot_dim;
   float r[8];
@@ -58,6 +75,10 @@ __device__ __forceinline__ void rope_unit(const RopeParams &p, long long u) {
       out[i] = f32_to_bf16_bits(r[2 * i]) | (f32_to_bf16_bits(r[2 * i + 1]) << 16);
     *(uint4 *)((uint16_t *)p.y + off) = make_uint4(out[0], out[1], out[2], out[3]);
   }
+}
+
+__device__ __forceinline__ void rope_unit(const RopeParams &p, long long u) {
+  rope_finish(p, u, rope_load(p, u));
 }
 
 // Units (8-element groups) of a rotation.

@@ -181,7 +181,8 @@ int fp4kv_cache_nbytes(const fp4kv_cache *c, size_t out[6]);
  */
 int fp4kv_cache_reset(const fp4kv_cache *c, void *stream);
 
-/* Bytes of device workspace fp4kv_quantize_append needs (constant). */
+/* Bytes of device workspace fp4kv_quantize_append and fp4kv_rope_append
+ * need (constant, 76,288). */
 size_t fp4kv_append_workspace_bytes(void);
 
 /*
@@ -368,17 +369,33 @@ int fp4kv_rope_rel_frames(const fp4kv_cache *c, const void *x, int in_dtype, voi
                           void *stream);
 
 /*
- * fp4kv_rope_append - the two codec steps of one chunk in one call and two
- * kernels: the rotation of the chunk's queries (fp4kv_rope_rel_frames of q
- * into q_rot) and the append of its keys and values
- * (fp4kv_quantize_append with tscale_in = NULL).  The first kernel takes the
- * partial maxima of K and V and rotates part of the queries, the second
- * encodes K and V into the cache and rotates the rest of the queries
- * ("fused RoPE" and "in-place quantized KV-cache updates", hysenlabs.com,
- * section "NVFP4, sequence parallel and the async decode path").  Results are bit for bit those of the two separate calls.
+ * fp4kv_rope_append - the two codec steps of one chunk in one call: the
+ * rotation of the chunk's queries (fp4kv_rope_rel_frames of q into q_rot)
+ * and the append of its keys and values (fp4kv_quantize_append with
+ * tscale_in = NULL) ("fused RoPE" and "in-place quantized KV-cache
+ * updates", hysenlabs.com, section "NVFP4, sequence parallel and the async
+ * decode path").  Results are bit for bit those of the two separate calls.
+ *   - bf16 keys and values: one kernel over a grid that the device holds
+ *     at once.  Every thread reads 4 tokens of one 16-element block of K or
+ *     V once and keeps them in registers; the workgroups publish partial
+ *     maxima, meet at a grid barrier kept in the workspace (rotating the
+ *     queries while they wait), then encode what they hold.  When the
+ *     chunk has more such items than that grid has threads, the two-kernel
+ *     form below runs instead.
+ *   - float32 keys and values: two kernels, the first taking the partial
+ *     maxima of K and V and rotating part of the queries, the second
+ *     encoding K and V and rotating the rest.
  * Arguments as in those calls; the cache must have format
  * FP4KV_FORMAT_NVFP4_V1 (FP4KV_EINVAL otherwise).  q_rot must not be k or v
  * (q_rot may be q when the dtypes match).
+ *   workspace   as for fp4kv_quantize_append, but its last 8448 bytes (the
+ *               grid barrier) must hold zeros before the first call that
+ *               uses the workspace; every call leaves them so.  If the
+ *               device cannot hold the whole grid (other work keeps it from
+ *               starting) a workgroup gives up its wait after about 10^6
+ *               polls and skips its encode instead of hanging; the 32-bit
+ *               word at byte offset fp4kv_append_workspace_bytes() - 128
+ *               is then set to 1 (it is never cleared by the library).
  */
 int fp4kv_rope_append(const fp4kv_cache *c, const void *q, int q_dtype, void *q_rot,
                       int q_rot_dtype, const void *k, const void *v, int kv_dtype, int32_t frame0,

@@ -58,7 +58,7 @@ def _desc(**kw):
 
 def test_strerror_and_version():
     lib = _lib.load()
-    assert lib.fp4kv_abi_version() == 5
+    assert lib.fp4kv_abi_version() == 6
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.fp4kv_strerror(st)
     assert lib.fp4kv_append_workspace_bytes() >= 64 * 33 * 4   # re-rotation maxima

@@ -5,9 +5,11 @@ prologue, through the C ABI:
     position (also across shot cuts with per-shot sinks, where positions are
     not consecutive): bit for bit what fp4kv_rope_rel gives with those
     positions, and within float32 error of the oracle's float64 rotation;
-  * fp4kv_rope_append (the queries' rotation and the append in two kernels)
-    leaves the same cache bytes and rotated queries as the separate calls,
-    step after step, on the small streams and on the full-size layers.
+  * fp4kv_rope_append (the queries' rotation and the append: one pass for
+    bf16 inputs, two kernels for float32) leaves the same cache bytes and
+    rotated queries as the separate calls, step after step, on the small
+    streams and on the full-size layers, and leaves its grid barrier's
+    workspace words clear.
 """
 import numpy as np
 import pytest
@@ -81,6 +83,20 @@ def _prologue_stream(w, steps, per_shot=False, check=None):
             ba, bb = _bytes(a), _bytes(b)
             for name in ba:
                 assert ba[name] == bb[name], (w.name, c, name)
+    _barrier_words_clear(b)
+
+
+def _barrier_words_clear(gc):
+    """The one-pass prologue's grid barrier (the workspace's last 33 lines of
+    64 words: per group an arrival count (word 0) and a phase (word 32), then
+    the count of complete groups and the error word) is left with zero counts
+    and no error after every call, and all phases agree (each call flips them
+    all)."""
+    ws = gc.workspace.cpu().numpy().view(np.uint32)
+    bar = ws[-33 * 64:].reshape(33, 64)
+    assert not bar[:, 0].any(), bar[:, 0]
+    assert bar[32, 32] == 0
+    assert bar[:32, 32].min() == bar[:32, 32].max() and bar[0, 32] in (0, 1), bar[:32, 32]
 
 
 def test_rope_append_equals_separate_calls_small():
