@@ -112,3 +112,14 @@ def test_rope_append_equals_separate_calls_full_size(name):
     w = wl.WORKLOADS[name]
     steps = 8 if name == "long" else min(w.n_chunks, (w.S + w.W) // w.C + 1)
     _prologue_stream(w, steps, per_shot=name == "l5b_shots", check={0, steps - 1})
+
+
+def test_rope_append_large_chunk_takes_the_two_kernel_form():
+    """A bf16 chunk with more items (4 kept tokens x one 16-element block of
+    K or V: 524,288 here) than the one-pass grid has threads on MI355X
+    (1024 workgroups of 256) runs the two-kernel form: same bytes as the
+    separate calls, and the barrier words untouched."""
+    w = wl.Workload("wide", H=32, D=128, T=64, C=64, S=0, W=64, n_frames=64, seed=77,
+                    dtype="bf16", outlier_p=0.01, outlier_scale=20.0)
+    assert 2 * w.H * w.n_frames * (w.T // 8) * (w.D // 16) * 2 == 524288
+    _prologue_stream(w, 1)
