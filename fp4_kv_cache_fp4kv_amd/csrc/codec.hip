@@ -603,6 +603,9 @@ __global__ __launch_bounds__(kThreads, 4) void prologue_kernel(RopeParams rp, Ap
       if (old_top == (uint32_t)n_groups - 1u) {   // every group: reset, release all
         __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // every group's phase flips: all phases are equal between calls
+        // (zero at first, and each call flips every group of its grid, whose
+        // size is fixed per device)
         for (int g2 = 0; g2 < n_groups; ++g2)
           __hip_atomic_store(p.ws_bar + g2 * kBarLine + kWsBarPhase, phase0 ^ 1u,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -805,12 +808,13 @@ __global__ void reset_kernel(int32_t *slot_frame, int32_t *slot_shot, float *kt,
 }  // namespace
 
 // ---- append workspace for callers that cannot allocate ----
-// fp4kv_quantize_append_noalloc keeps the append's workspace (partial maxima
-// between its two kernels) in this array instead of a caller buffer.  Each
-// device holds its own copy for the life of the process; every call on a
-// device shares it, so calls that overlap in time on one device race.  No
-// part of it needs clearing: the amax kernel writes every partial maximum
-// the encode kernel reads.
+// fp4kv_quantize_append_noalloc keeps the append's workspace (partial maxima,
+// and the one-pass kernel's grid barrier) in this array instead of a caller
+// buffer.  Each device holds its own copy for the life of the process; every
+// call on a device shares it, so calls that overlap in time on one device
+// race.  Nothing needs clearing between calls: every partial maximum read is
+// written by the same call first, and the barrier words, zero at load, are
+// left at zero counts by every call.
 static __device__ __align__(256) uint8_t scratch[kWsBytes];
 
 namespace {
@@ -872,26 +876,6 @@ hipError_t launch_encode(const AppendParams &p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_append(const AppendParams &p_in, hipStream_t s) {
-  AppendParams p = p_in;
-  append_blocks(p);
-  if (p.bf16_cache) {
-    const long long k_units = (long long)p.n_frames * p.Tc * p.H * (p.D >> 3);
-    const long long k_blocks = (k_units + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(store_bf16_kernel, dim3((unsigned)(p.v_blocks + k_blocks)), dim3(kThreads),
-                       0, s, p);
-    return hipGetLastError();
-  }
-  p.amax_tensors = (p.n_frames > 0 && !p.tscale_in) ? 2 : 0;
-  const int amax_y = p.amax_tensors + p.rr_slots;
-  if (amax_y > 0) {
-    hipLaunchKernelGGL(amax_kernel, dim3(kAmaxBlocks, amax_y), dim3(kThreads), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return launch_encode(p, s);
-}
-
 namespace {
 // Workgroups of prologue_kernel that one device holds at once: compute
 // units x resident workgroups per unit (resolved once per device).
@@ -916,28 +900,68 @@ hipError_t prologue_resident(int *out) {
   *out = g_resident[dev];
   return hipSuccess;
 }
+
+// The one-pass kernel for an NVFP4 append of bf16 inputs with computed
+// tensor scales (and the rotation rp, which may have no tokens), when every
+// item has a thread in a grid that the device holds at once.  The grid is
+// all that fits, so the rotation's reads in flight fill every compute unit
+// (workgroups past the items rotate only).  *done tells whether it ran.
+hipError_t launch_one_pass(const RopeParams &rp, const AppendParams &ap, hipStream_t s,
+                           bool *done) {
+  *done = false;
+  if (!ap.in_bf16 || ap.tscale_in || ap.bf16_cache || ap.rotate_keys || ap.rr_slots > 0 ||
+      ap.n_frames < 1)
+    return hipSuccess;
+  int resident = 0;
+  hipError_t e = prologue_resident(&resident);
+  if (e != hipSuccess) return e;
+  const long long items = prologue_k_items(ap) + prologue_v_items(ap);
+  const long long need = (items + kThreads - 1) / kThreads;
+  const long long grid = resident < kPrologueMaxGrid ? resident : kPrologueMaxGrid;
+  if (resident <= 0 || need > grid) return hipSuccess;
+  hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, rp, ap);
+  *done = true;
+  return hipGetLastError();
+}
 }  // namespace
+
+hipError_t launch_append(const AppendParams &p_in, hipStream_t s) {
+  AppendParams p = p_in;
+  append_blocks(p);
+  if (p.bf16_cache) {
+    const long long k_units = (long long)p.n_frames * p.Tc * p.H * (p.D >> 3);
+    const long long k_blocks = (k_units + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(store_bf16_kernel, dim3((unsigned)(p.v_blocks + k_blocks)), dim3(kThreads),
+                       0, s, p);
+    return hipGetLastError();
+  }
+  p.amax_tensors = (p.n_frames > 0 && !p.tscale_in) ? 2 : 0;
+  {
+    RopeParams none = {};   // no queries to rotate
+    none.D = p.D;
+    none.H = p.H;
+    none.T = p.T;
+    bool done = false;
+    hipError_t e = launch_one_pass(none, p, s, &done);
+    if (e != hipSuccess || done) return e;
+  }
+  const int amax_y = p.amax_tensors + p.rr_slots;
+  if (amax_y > 0) {
+    hipLaunchKernelGGL(amax_kernel, dim3(kAmaxBlocks, amax_y), dim3(kThreads), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_encode(p, s);
+}
+
 
 hipError_t launch_rope_append(const RopeParams &rp, const AppendParams &ap_in, hipStream_t s) {
   AppendParams ap = ap_in;   // NVFP4 cache, computed tensor scales, no window move
   append_blocks(ap);
   ap.amax_tensors = 2;
-  if (ap.in_bf16) {
-    // One pass when every item has a thread in a grid that the device
-    // holds at once; the grid is all that fits, so the rotation's reads in
-    // flight fill every compute unit (workgroups past the items rotate
-    // only).
-    int resident = 0;
-    hipError_t e = prologue_resident(&resident);
-    if (e != hipSuccess) return e;
-    const long long items = prologue_k_items(ap) + prologue_v_items(ap);
-    const long long need = (items + kThreads - 1) / kThreads;
-    const long long grid = resident < kPrologueMaxGrid ? resident : kPrologueMaxGrid;
-    if (resident > 0 && need <= grid) {
-      hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, rp, ap);
-      return hipGetLastError();
-    }
-  }
+  bool done = false;
+  hipError_t e = launch_one_pass(rp, ap, s, &done);
+  if (e != hipSuccess || done) return e;
   const long long n = rope_units(rp);
   const long long n1 = n * kRopeFirstEighths / 8;   // units rotated in the first kernel
   auto blocks_for = [](long long units) {
@@ -946,7 +970,7 @@ hipError_t launch_rope_append(const RopeParams &rp, const AppendParams &ap_in, h
   };
   hipLaunchKernelGGL(rope_amax_kernel, dim3((unsigned)(2 * kAmaxBlocks + blocks_for(n1))),
                      dim3(kThreads), 0, s, rp, ap, n1);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long enc = (long long)ap.v_blocks + ap.k_blocks;
   hipLaunchKernelGGL(encode_rope_kernel, dim3((unsigned)(enc + blocks_for(n - n1))),

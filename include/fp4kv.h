@@ -207,9 +207,18 @@ size_t fp4kv_append_workspace_bytes(void);
  *               > 0), or NULL to compute g = amax / 2688 over the kept tokens
  *               of each of K and V (g = 1 when amax = 0).
  *   workspace   device, fp4kv_append_workspace_bytes() bytes, 16-byte
- *               aligned, no initialization needed (it holds partial maxima
- *               between the call's two kernels).  Calls that overlap in time
- *               must use different workspaces.
+ *               aligned.  It holds the partial maxima of K and V and, for
+ *               bf16 inputs with computed tensor scales, the grid barrier of
+ *               the one-pass kernel in its last 8448 bytes, which must hold
+ *               zeros before the first call that uses the workspace (every
+ *               call leaves them so; the rest needs no initialization).
+ *               Calls that overlap in time must use different workspaces.
+ *
+ * Kernels: bf16 inputs with computed tensor scales (NVFP4 format, nothing
+ * stored rotated) take one kernel that reads K and V once, as in
+ * fp4kv_rope_append; float32 inputs, caller tensor scales, the other
+ * formats and chunks too large for that kernel's grid take two (partial
+ * maxima, then the encode).
  *
  * Encoding, per 16-element block b along D of one (token, head) row, all in
  * IEEE float32 with round-to-nearest-even:
@@ -388,14 +397,15 @@ int fp4kv_rope_rel_frames(const fp4kv_cache *c, const void *x, int in_dtype, voi
  * Arguments as in those calls; the cache must have format
  * FP4KV_FORMAT_NVFP4_V1 (FP4KV_EINVAL otherwise).  q_rot must not be k or v
  * (q_rot may be q when the dtypes match).
- *   workspace   as for fp4kv_quantize_append, but its last 8448 bytes (the
- *               grid barrier) must hold zeros before the first call that
- *               uses the workspace; every call leaves them so.  If the
- *               device cannot hold the whole grid (other work keeps it from
- *               starting) a workgroup gives up its wait after about 10^6
- *               polls and skips its encode instead of hanging; the 32-bit
- *               word at byte offset fp4kv_append_workspace_bytes() - 128
- *               is then set to 1 (it is never cleared by the library).
+ *   workspace   as for fp4kv_quantize_append (its last 8448 bytes, the
+ *               grid barrier, hold zeros before the first use).  If the
+ *               device cannot hold the whole one-pass grid (other work keeps
+ *               part of it from starting) a workgroup gives up its wait
+ *               after about 10^6 polls and skips its encode instead of
+ *               hanging; the 32-bit word at byte offset
+ *               fp4kv_append_workspace_bytes() - 128 is then set to 1 (the
+ *               library never clears it).  The same holds for
+ *               fp4kv_quantize_append and its no-alloc variant.
  */
 int fp4kv_rope_append(const fp4kv_cache *c, const void *q, int q_dtype, void *q_rot,
                       int q_rot_dtype, const void *k, const void *v, int kv_dtype, int32_t frame0,

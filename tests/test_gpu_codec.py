@@ -146,16 +146,26 @@ def test_codec_zero_tensor_gets_unit_scale():
     assert oc.k_tscale[0] == 1.0 and oc.slot_shot[0] == 5
 
 
-def test_workspace_needs_no_initialization():
-    """Garbage in the workspace does not change the encoding."""
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_workspace_needs_no_initialization(dtype):
+    """Garbage in the workspace outside its last 8448 bytes (the one-pass
+    kernel's grid barrier, which must start at zero) does not change the
+    encoding: float32 inputs take the two-kernel form, bf16 inputs the one
+    pass, which leaves the barrier words at zero counts."""
     from fp4_kv_cache_fp4kv_amd import api
-    w = wl.TINY
+    w = wl.Workload("ws", H=3, D=64, T=24, C=2, S=1, W=4, n_frames=12, seed=13, dtype=dtype,
+                    outlier_p=0.01, outlier_scale=20.0)
     gc, oc = gpu_cache(w), OracleCache.for_workload(w)
     gc.workspace.fill_(0xA7)
-    (_, _), (k, kb), (v, vb) = step_inputs(w, 0)
-    api.quantize_append(gc, device_tensor(k, kb), device_tensor(v, vb), 0, 2, [0, 0])
-    oc.append(k, v, 0, 2, [0, 0])
-    assert not compare_cache(gc, oc)
+    gc.workspace[-8448:].zero_()
+    for c in range(3):
+        f0, n = w.chunk_frames(c)
+        (_, _), (k, kb), (v, vb) = step_inputs(w, c)
+        api.quantize_append(gc, device_tensor(k, kb), device_tensor(v, vb), f0, n, [0] * n)
+        oc.append(k, v, f0, n, [0] * n)
+        assert not compare_cache(gc, oc), c
+    bar = gc.workspace.cpu().numpy().view(np.uint32)[-33 * 64:].reshape(33, 64)
+    assert not bar[:, 0].any() and bar[32, 32] == 0
 
 
 def test_bulk_reappend_kv_recache():
