@@ -98,8 +98,10 @@ def copy_calibration(nbytes):
 
 def codec_sweep(w):
     """Append bandwidth against size, next to what a plain device copy reaches
-    at similar sizes: the ceiling a two-pass append can approach at a given
-    size.  Both are timed with HIP events over 30 calls on the same resident
+    at similar sizes.  A chunk of the step's size takes the one-pass append
+    (K and V read once); the larger ones, more than its grid holds, take the
+    two kernels (partial maxima, then the encode, which reads K and V a
+    second time).  Both are timed with HIP events over 30 calls on the same resident
     inputs, so sizes up to ~100 MB stay in the 256 MB Infinity Cache between
     calls (hot numbers); the benchmark's own step rotates 8 input sets, more
     than the Infinity Cache holds."""
