@@ -11,6 +11,7 @@
 // the same ring layout.  For caches that store keys rotated, the same two
 // kernels also turn the appended keys by their positions and re-encode the
 // window slots a window move turns (grid rows / workgroups of their own).
+#include <cstdlib>
 #include <mutex>
 
 #include "fp4kv_device.hpp"
@@ -72,18 +73,16 @@ __device__ __forceinline__ void load_key_block(const AppendParams &p, int j, int
 // workgroup's share of the slot's (key row, block) pairs.
 __device__ __forceinline__ void rerot_amax(const AppendParams &p, int s, uint32_t *red);
 
-// Partial max |x| of appended tensor y (0 = K, 1 = V) over the kept tokens,
-// taken by workgroup bx of nbx and stored as ws_partial[y][bx].
-__device__ __forceinline__ void amax_part(const AppendParams &p, int y, int bx, int nbx,
-                                          uint32_t *red) {
+// This thread's max |x| (bit pattern) over the 16-byte chunks first,
+// first + step, ... of appended tensor y (0 = K, 1 = V), kept tokens only.
+__device__ __forceinline__ uint32_t amax_chunks(const AppendParams &p, int y, uint32_t first,
+                                                uint32_t step) {
   const bool bf16 = p.in_bf16;
   const uint32_t row_chunks = (uint32_t)(p.H * p.D * (bf16 ? 2 : 4) / 16);  // one token
   const uint32_t n_chunks = (uint32_t)(p.n_frames * p.Tc) * row_chunks;
   const uint4 *base = (const uint4 *)p.x[y];
-  const uint32_t step = (uint32_t)nbx * kThreads;
   uint32_t m = 0;
-  for (uint32_t c0 = (uint32_t)bx * kThreads + threadIdx.x; c0 < n_chunks;
-       c0 += step * kAmaxUnroll) {
+  for (uint32_t c0 = first; c0 < n_chunks; c0 += step * kAmaxUnroll) {
     uint4 v[kAmaxUnroll];
 #pragma unroll
     for (int k = 0; k < kAmaxUnroll; ++k) {
@@ -100,6 +99,14 @@ __device__ __forceinline__ void amax_part(const AppendParams &p, int y, int bx, 
     for (int k = 0; k < kAmaxUnroll; ++k) m = fold_max(m, v[k], bf16);
   }
   if (bf16) m = max(m & 0xFFFFu, m >> 16) << 16;   // bf16 bits -> float32 bits
+  return m;
+}
+
+// Partial max |x| of appended tensor y (0 = K, 1 = V) over the kept tokens,
+// taken by workgroup bx of nbx and stored as ws_partial[y][bx].
+__device__ __forceinline__ void amax_part(const AppendParams &p, int y, int bx, int nbx,
+                                          uint32_t *red) {
+  uint32_t m = amax_chunks(p, y, (uint32_t)bx * kThreads + threadIdx.x, (uint32_t)nbx * kThreads);
   m = block_max_u32(m, red);
   if (threadIdx.x == 0) p.ws_partial[y * kAmaxBlocks + bx] = m;
 }
@@ -491,8 +498,13 @@ __global__ __launch_bounds__(kThreads) void encode_rope_kernel(AppendParams p, R
 // every group's phase word, which only that group's workgroups poll.  Each
 // count is cleared by its last arrival, so the workspace is left as found;
 // it must hold zeros before its first use.  A wait that exceeds
-// kBarrierSpins polls gives up: the workgroup sets the error word and skips
-// its encode instead of hanging.
+// kBarrierSpins polls (part of the grid kept from starting, e.g. by another
+// such grid on a concurrent stream) gives up: the workgroup sets the error
+// word and takes the maxima of K and V over all their elements itself, which
+// gives the same tensor scales and needs no other workgroup, so every call
+// completes with the same bytes.  The environment variable
+// FP4KV_BARRIER_SPINS, read on every call, sets a lower limit, so that tests
+// can force this path.
 constexpr int kBarrierSpins = 1 << 20;
 constexpr int kSc1 = 16;   // cache-policy operand: sc1, a device-coherent access
 constexpr uint32_t kBufferWord3 = 0x00020000u;
@@ -631,7 +643,7 @@ __global__ __launch_bounds__(kThreads, 4) void prologue_kernel(RopeParams rp, Ap
     int ok = 1;
     for (int it = 0; __hip_atomic_load(phase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == phase0;
          ++it) {
-      if (it >= kBarrierSpins) {
+      if (it >= p.spin_limit) {
         __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ok = 0;
         break;
@@ -641,11 +653,15 @@ __global__ __launch_bounds__(kThreads, 4) void prologue_kernel(RopeParams rp, Ap
     go = ok;
   }
   __syncthreads();
-  if (!go) return;
   uint32_t ak = 0u, av = 0u;
-  for (int i = threadIdx.x; i < G; i += kThreads) {
-    ak = max(ak, __builtin_amdgcn_raw_buffer_load_b32(part, 4 * i, 0, kSc1));
-    av = max(av, __builtin_amdgcn_raw_buffer_load_b32(part, 4 * (G + i), 0, kSc1));
+  if (go) {
+    for (int i = threadIdx.x; i < G; i += kThreads) {
+      ak = max(ak, __builtin_amdgcn_raw_buffer_load_b32(part, 4 * i, 0, kSc1));
+      av = max(av, __builtin_amdgcn_raw_buffer_load_b32(part, 4 * (G + i), 0, kSc1));
+    }
+  } else {   // the wait gave up: the maxima over every element, alone
+    ak = amax_chunks(p, 0, threadIdx.x, kThreads);
+    av = amax_chunks(p, 1, threadIdx.x, kThreads);
   }
   block_max2_u32(ak, av, red);
   const float amax_k = __uint_as_float(ak), amax_v = __uint_as_float(av);
@@ -919,7 +935,14 @@ hipError_t launch_one_pass(const RopeParams &rp, const AppendParams &ap, hipStre
   const long long need = (items + kThreads - 1) / kThreads;
   const long long grid = resident < kPrologueMaxGrid ? resident : kPrologueMaxGrid;
   if (resident <= 0 || need > grid) return hipSuccess;
-  hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, rp, ap);
+  AppendParams a = ap;
+  a.spin_limit = kBarrierSpins;
+  if (const char *env = getenv("FP4KV_BARRIER_SPINS")) {
+    char *end = nullptr;
+    const long v = strtol(env, &end, 10);
+    if (end != env && v >= 0 && v <= kBarrierSpins) a.spin_limit = (int)v;
+  }
+  hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, rp, a);
   *done = true;
   return hipGetLastError();
 }

@@ -43,6 +43,7 @@ struct AppendParams {
   const float *tscale_in;  // device [2] or null
   uint32_t *ws_partial;    // [2][kAmaxBlocks]
   uint32_t *ws_bar;        // grid barrier words of the one-pass prologue
+  int spin_limit;          // polls before a one-pass barrier wait gives up
   int H, D, T, stride, Tc, Tv, S, W, n_slots, frame0, n_frames;
   int in_bf16;
   int bf16_cache;          // FP4KV_FORMAT_BF16_V1: store bf16, no quantization

@@ -398,14 +398,18 @@ int fp4kv_rope_rel_frames(const fp4kv_cache *c, const void *x, int in_dtype, voi
  * FP4KV_FORMAT_NVFP4_V1 (FP4KV_EINVAL otherwise).  q_rot must not be k or v
  * (q_rot may be q when the dtypes match).
  *   workspace   as for fp4kv_quantize_append (its last 8448 bytes, the
- *               grid barrier, hold zeros before the first use).  If the
- *               device cannot hold the whole one-pass grid (other work keeps
- *               part of it from starting) a workgroup gives up its wait
- *               after about 10^6 polls and skips its encode instead of
- *               hanging; the 32-bit word at byte offset
- *               fp4kv_append_workspace_bytes() - 128 is then set to 1 (the
- *               library never clears it).  The same holds for
- *               fp4kv_quantize_append and its no-alloc variant.
+ *               grid barrier, hold zeros before the first use).  If part of
+ *               the one-pass grid cannot start (other work on the device,
+ *               for instance another one-pass call on a concurrent stream),
+ *               a workgroup gives up its wait after about 10^6 polls and
+ *               takes the maxima of K and V over all their elements itself:
+ *               the bytes are the same, the call only slower.  The 32-bit
+ *               word at byte offset fp4kv_append_workspace_bytes() - 128 is
+ *               then set to 1 (the library never clears it).  The
+ *               environment variable FP4KV_BARRIER_SPINS (a number of
+ *               polls, read on every call) lowers the limit, for tests.  The
+ *               same holds for fp4kv_quantize_append and its no-alloc
+ *               variant.
  */
 int fp4kv_rope_append(const fp4kv_cache *c, const void *q, int q_dtype, void *q_rot,
                       int q_rot_dtype, const void *k, const void *v, int kv_dtype, int32_t frame0,

@@ -123,3 +123,36 @@ def test_rope_append_large_chunk_takes_the_two_kernel_form():
                     dtype="bf16", outlier_p=0.01, outlier_scale=20.0)
     assert 2 * w.H * w.n_frames * (w.T // 8) * (w.D // 16) * 2 == 524288
     _prologue_stream(w, 1)
+
+
+def test_one_pass_wait_that_gives_up_keeps_the_bytes(monkeypatch):
+    """The one-pass kernel's barrier wait is bounded.  With the limit forced
+    to 0 polls from the host (FP4KV_BARRIER_SPINS), workgroups give up their
+    wait at once, take the tensor maxima over all of K and V themselves and
+    encode: every kernel ends normally, the cache stays bit-exact against the
+    oracle step after step, the error word is set, and the barrier counts
+    still end at zero."""
+    from fp4_kv_cache_fp4kv_amd import api
+    from oracle.stream import OracleCache
+    from streams import compare_cache
+    w = wl.Workload("giveup", H=3, D=128, T=40, C=2, S=1, W=4, n_frames=10, seed=83,
+                    dtype="bf16", outlier_p=0.01, outlier_scale=20.0)
+    monkeypatch.setenv("FP4KV_BARRIER_SPINS", "0")
+    gc = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride)
+    oc = OracleCache.for_workload(w)
+    for c in range(w.n_chunks):
+        f0, n = w.chunk_frames(c)
+        (q, qb), (k, kb), (v, vb) = step_inputs(w, c)
+        say(f"rope_append, wait limit 0, step {c}")
+        qd, kd, vd = device_tensor(q, qb), device_tensor(k, kb), device_tensor(v, vb)
+        got = api.rope_append(gc, qd, kd, vd, f0, n, [0] * n)
+        ref = api.rope_rel_frames(gc, qd, f0, n)
+        api.quantize_append(gc, kd, vd, f0, n, [0] * n)   # the one-pass append, same limit
+        torch.cuda.synchronize()
+        oc.append(k, v, f0, n, [0] * n)
+        assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), c
+        assert not compare_cache(gc, oc), c
+    ws = gc.workspace.cpu().numpy().view(np.uint32)
+    bar = ws[-33 * 64:].reshape(33, 64)
+    assert not bar[:, 0].any()
+    assert bar[32, 32] == 1   # at least one wait gave up
