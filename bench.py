@@ -279,7 +279,7 @@ def measure(w, steps, warmup, sets, kv="nvfp4", sink_per_shot=False, workgroups=
         if record:
             e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             e[0].record()
-        if fused:   # the queries' rotation and the append: two kernels
+        if fused:   # the queries' rotation and the append in one call (one kernel here)
             api.rope_append(gc, q, k, v, f0, w.C, shots, shot_starts=fss, q_out=qrot)
         elif rot:   # turn the surviving window keys, store the new keys rotated
             api.quantize_append_rotated(gc, k, v, f0, w.C, shots, shot_starts=fss)

@@ -319,8 +319,8 @@ def rope_append(cache: FP4KVCache, q: torch.Tensor, k: torch.Tensor, v: torch.Te
                 q_out: Optional[torch.Tensor] = None, q_out_dtype=torch.float32) -> torch.Tensor:
     """fp4kv_rope_append on the current stream: rotate the chunk's queries
     (as rope_rel_frames) and append its keys and values (as quantize_append
-    with computed tensor scales) in two kernels.  Returns the rotated
-    queries."""
+    with computed tensor scales) in one call: one kernel for bfloat16 keys
+    and values, two for float32.  Returns the rotated queries."""
     if cache.kv_format != "nvfp4":
         raise ValueError("rope_append needs a cache with kv_format 'nvfp4'")
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
