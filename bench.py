@@ -255,7 +255,8 @@ def shot_start_fn(w):
 def measure(w, steps, warmup, sets, kv="nvfp4", sink_per_shot=False, workgroups=0):
     """Steady-state steps of one layer: the cache update (with the queries'
     rotation when it is fused) and attention, each bracketed by HIP events
-    on the launch stream; the whole K steps bracketed by synchronizations."""
+    on the launch stream (one event between consecutive kernels); the whole
+    K steps bracketed by synchronizations."""
     import torch
 
     from fp4_kv_cache_fp4kv_amd import api
@@ -269,16 +270,17 @@ def measure(w, steps, warmup, sets, kv="nvfp4", sink_per_shot=False, workgroups=
     rot = kv == "nvfp4_rot"
     fused = kv == "nvfp4"   # one rope_append call: rotation fused with the amax pass
     first = -(-(w.S + w.W) // w.C)       # first chunk step with a full window
-    ev = {k: [] for k in ("a0", "a1", "c0", "c1")}
+    # Event chain over the timed steps: b_t | cache update | m_t | attention
+    # | b_{t+1}.  Each event ends one kernel's interval and starts the next
+    # (they are back to back on the stream); b_0 and b_K are the events that
+    # bracket the whole timed region.
+    ev = {"b": [], "m": []}
 
     def step(c, record):
         q, k, v = sets[c % len(sets)]
         f0 = c * w.C
         shots = [w.shot_of(f) for f in range(f0, f0 + w.C)]
         fss = [shot_start(f) for f in range(f0, f0 + w.C)] if sink_per_shot else None
-        if record:
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            e[0].record()
         if fused:   # the queries' rotation and the append in one call (one kernel here)
             api.rope_append(gc, q, k, v, f0, w.C, shots, shot_starts=fss, q_out=qrot)
         elif rot:   # turn the surviving window keys, store the new keys rotated
@@ -288,13 +290,12 @@ def measure(w, steps, warmup, sets, kv="nvfp4", sink_per_shot=False, workgroups=
         if not fused:
             api.rope_rel_frames(gc, q, f0, w.C, shot_starts=fss, out=qrot)
         if record:
-            e[1].record()
-            e[2].record()
+            ev["m"].append(torch.cuda.Event(enable_timing=True))
+            ev["m"][-1].record()
         api.attention_chunk(gc, qrot, f0, w.C, shots, out=out, n_workgroups=workgroups)
-        if record:
-            e[3].record()
-            ev["c0"].append(e[0]); ev["c1"].append(e[1])
-            ev["a0"].append(e[2]); ev["a1"].append(e[3])
+        if record and len(ev["m"]) < steps:   # the last step ends at t1
+            ev["b"].append(torch.cuda.Event(enable_timing=True))
+            ev["b"][-1].record()
 
     for c in range(first):                # fill the sink and window
         step(c, False)
@@ -312,8 +313,9 @@ def measure(w, steps, warmup, sets, kv="nvfp4", sink_per_shot=False, workgroups=
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
-    attn_each = sorted(a.elapsed_time(b) for a, b in zip(ev["a0"], ev["a1"]))
-    update_ms = sum(a.elapsed_time(b) for a, b in zip(ev["c0"], ev["c1"])) / steps
+    bounds = [t0] + ev["b"] + [t1]                # b_0 .. b_K
+    attn_each = sorted(m.elapsed_time(b) for m, b in zip(ev["m"], bounds[1:]))
+    update_ms = sum(b.elapsed_time(m) for b, m in zip(bounds[:-1], ev["m"])) / steps
     f0s = [(c - steps + i) * w.C for i in range(steps)]
     # useful FLOP: only the (query frame, key frame) pairs the masks keep,
     # averaged over the timed steps (equal to 4 H Nq Nk D without shots)
