@@ -3,11 +3,13 @@
 One step = the whole hot path for one chunk of one attention layer, in
 steady state (sink + full window):
     fp4kv_rope_append(Q, K, V) -> fp4kv_attention_chunk
-(the queries' rotation fused with the append's amax pass, then the encode,
-then attention) on seeded synthetic inputs already resident in device
-memory.  The stream keeps going (the ring wraps); inputs rotate over 16
-sets (8 seeded draws and their negations, 690 MB for the 1.3B-like layer,
-more than the 256 MB Infinity Cache holds).
+(the queries' rotation and the NVFP4 append in one pass for these bf16
+inputs, then attention) on seeded synthetic inputs already resident in
+device memory.  The stream keeps going (the ring wraps); inputs rotate over
+16 sets (8 seeded draws and their negations, 690 MB for the 1.3B-like
+layer, more than the 256 MB Infinity Cache holds).  Before the W warmup
+steps the cache is filled by streaming at least FILL_STEPS untimed steps,
+which also outlast the clock ramp that follows the host-side input draw.
 
 Workload (default): one layer shaped like the 1.3B generator: 12 heads,
 head_dim 128, 1560 tokens/frame, chunk 3 frames, sink 3 + window 12 frames,
@@ -17,7 +19,7 @@ Printed: one JSON line.  value = frames/s of one layer = C * K / time of K
 steps.  roofline = the attention kernel (the dominant one): algorithmic
 FLOP per launch (4*D per (query, key) pair the masks keep) / its mean
 duration from HIP events on the launch stream, against the 2.5 PFLOP/s
-dense f16/bf16 MFMA peak.  roofline_codec = the step's codec kernels as
+dense f16/bf16 MFMA peak.  roofline_codec = the step's codec kernel as
 timed inside the steps (rotation + append): algorithmic bytes (queries read
 and written as float32, kept K and V read once, codes and scales written
 once) / their mean duration, against 8 TB/s.  codec = the append alone and
@@ -46,6 +48,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "FP4-KV chunk attention latent frames/s per layer; HBM GB/s & MFMA % of peak"
+# Untimed steps that fill the cache before the warmup steps (at least the
+# steps to fill the sink and window): ~55 ms of device time on the 1.3B-like
+# layer, past the clock ramp that follows the host-side input draw.
+FILL_STEPS = 64
 
 
 def parse():
@@ -297,9 +303,14 @@ def measure(w, steps, warmup, sets, kv="nvfp4", sink_per_shot=False, workgroups=
             ev["b"].append(torch.cuda.Event(enable_timing=True))
             ev["b"][-1].record()
 
-    for c in range(first):                # fill the sink and window
+    # Fill the sink and window, streaming at least FILL_STEPS steps: the
+    # clocks ramp for ~25 ms after the host-side input draw leaves the device
+    # idle, and the fill is where that ramp is spent (the W warmup steps and
+    # the K timed steps follow as asked).
+    n_fill = max(first, FILL_STEPS)
+    for c in range(n_fill):
         step(c, False)
-    c = first
+    c = n_fill
     for _ in range(warmup):
         step(c, False)
         c += 1
@@ -334,7 +345,7 @@ def measure(w, steps, warmup, sets, kv="nvfp4", sink_per_shot=False, workgroups=
         key_frame = w.H * w.Tc * (w.D // 2 + w.D // 16)
         update_bytes += 2.0 * key_frame * sum(surv) / len(surv)
     del gc
-    return {"ms_step": ms_step, "attn_ms": attn_ms, "attn_each": attn_each,
+    return {"ms_step": ms_step, "attn_ms": attn_ms, "attn_each": attn_each, "fill": n_fill,
             "update_ms": update_ms, "update_bytes": update_bytes, "flops": flops,
             "pairs": sum(pairs) / len(pairs)}
 
@@ -478,7 +489,7 @@ def main():
         "config": {"workload": workload_desc(w), "kv_format": args.kv,
                    "sink": "per_shot" if args.sink_per_shot else "stream", "query_rows": Nq,
                    "workgroups": args.workgroups or "default",
-                   "keys": Nk, "input_sets": len(sets),
+                   "keys": Nk, "input_sets": len(sets), "fill_steps": m["fill"],
                    "frames_per_step": w.C, "attention_ms": round(m["attn_ms"], 4),
                    "attention_only_frames_per_s": round(w.C / (m["attn_ms"] * 1e-3), 1),
                    "attention_ms_p10_p50_p90": [round(pct(m["attn_each"], q), 4)
