@@ -156,3 +156,47 @@ def test_one_pass_wait_that_gives_up_keeps_the_bytes(monkeypatch):
     bar = ws[-33 * 64:].reshape(33, 64)
     assert not bar[:, 0].any()
     assert bar[32, 32] == 1   # at least one wait gave up
+
+
+def test_concurrent_one_pass_calls_on_two_streams(monkeypatch):
+    """Two fp4kv_rope_append calls of full-size 1.3B-like chunks (each grid as
+    large as the device holds at once) overlap on two streams, with their
+    own caches and workspaces.  Neither grid can then be sure to be resident
+    whole; a wait that gives up (its limit lowered from the host to 2000
+    polls so that it resolves in milliseconds) takes the maxima itself.
+    Every call must end normally with the bytes of the same calls made one
+    at a time."""
+    from fp4_kv_cache_fp4kv_amd import api
+    monkeypatch.setenv("FP4KV_BARRIER_SPINS", "2000")
+    w = wl.WORKLOADS["l13b"]
+    caches = [api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride) for _ in range(4)]
+    inputs = []
+    for c in range(2):
+        (q, qb), (k, kb), (v, vb) = step_inputs(w, c)
+        inputs.append((device_tensor(q, qb), device_tensor(k, kb), device_tensor(v, vb)))
+    # one at a time
+    ref = []
+    for i, (qd, kd, vd) in enumerate(inputs):
+        f0 = i * w.C
+        ref.append(api.rope_append(caches[i], qd, kd, vd, f0, w.C, [0] * w.C))
+    torch.cuda.synchronize()
+    # overlapped: the second call's stream does not wait for the first
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = []
+    for rep in range(3):
+        say(f"two concurrent one-pass calls, round {rep}")
+        torch.cuda.synchronize()
+        got = []
+        for i, (qd, kd, vd) in enumerate(inputs):
+            with torch.cuda.stream(streams[i]):
+                got.append(api.rope_append(caches[2 + i], qd, kd, vd, i * w.C, w.C, [0] * w.C))
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(got[i].view(torch.int32), ref[i].view(torch.int32)), (rep, i)
+            a, b = _bytes(caches[i]), _bytes(caches[2 + i])
+            for name in a:
+                assert a[name] == b[name], (rep, i, name)
+    for i, gc in enumerate(caches):
+        bar = gc.workspace.cpu().numpy().view(np.uint32)[-33 * 64:].reshape(33, 64)
+        assert not bar[:, 0].any(), bar[:, 0]
+        say(f"cache {i}: a wait gave up: {bool(bar[32, 32])}")
