@@ -8,8 +8,8 @@ inputs, then attention) on seeded synthetic inputs already resident in
 device memory.  The stream keeps going (the ring wraps); inputs rotate over
 16 sets (8 seeded draws and their negations, 690 MB for the 1.3B-like
 layer, more than the 256 MB Infinity Cache holds).  Before the W warmup
-steps the cache is filled by streaming at least FILL_STEPS untimed steps,
-which also outlast the clock ramp that follows the host-side input draw.
+steps the cache is filled by streaming untimed steps for at least FILL_MS,
+which outlasts the clock ramp that follows the host-side input draw.
 
 Workload (default): one layer shaped like the 1.3B generator: 12 heads,
 head_dim 128, 1560 tokens/frame, chunk 3 frames, sink 3 + window 12 frames,
@@ -48,10 +48,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "FP4-KV chunk attention latent frames/s per layer; HBM GB/s & MFMA % of peak"
-# Untimed steps that fill the cache before the warmup steps (at least the
-# steps to fill the sink and window): ~55 ms of device time on the 1.3B-like
-# layer, past the clock ramp that follows the host-side input draw.
-FILL_STEPS = 64
+# Wall time of the untimed steps that fill the cache before the warmup
+# steps (at least the steps that fill the sink and window): past the ~25 ms
+# clock ramp that follows the host-side input draw.
+FILL_MS = 60.0
 
 
 def parse():
@@ -303,14 +303,19 @@ def measure(w, steps, warmup, sets, kv="nvfp4", sink_per_shot=False, workgroups=
             ev["b"].append(torch.cuda.Event(enable_timing=True))
             ev["b"][-1].record()
 
-    # Fill the sink and window, streaming at least FILL_STEPS steps: the
-    # clocks ramp for ~25 ms after the host-side input draw leaves the device
-    # idle, and the fill is where that ramp is spent (the W warmup steps and
-    # the K timed steps follow as asked).
-    n_fill = max(first, FILL_STEPS)
-    for c in range(n_fill):
-        step(c, False)
-    c = n_fill
+    # Fill the sink and window, streaming untimed steps for at least FILL_MS
+    # of wall time: the clocks ramp for ~25 ms after the host-side input
+    # draw leaves the device idle, and the fill is where that ramp is spent
+    # (the W warmup steps and the K timed steps follow as asked).
+    import time
+    t_fill = time.perf_counter()
+    c = 0
+    while c < first or time.perf_counter() - t_fill < FILL_MS * 1e-3:
+        for _ in range(8):
+            step(c, False)
+            c += 1
+        torch.cuda.synchronize()
+    n_fill = c
     for _ in range(warmup):
         step(c, False)
         c += 1
