@@ -244,8 +244,10 @@ int fp4kv_quantize_append(const fp4kv_cache *c, const void *k, const void *v,
  * memory, one per device, for the life of the process (resolved on the first
  * call on each device).  The call allocates nothing.  All calls on one device
  * share that array: calls that overlap in time on one device race and must
- * be ordered by the caller (same stream or events).  No input size changes
- * the workspace it needs.  FP4KV_EDEVICE if the array's device address cannot
+ * be ordered by the caller (same stream or events).  The array is zero when
+ * the library is loaded, which the one-pass kernel's barrier words need, and
+ * every call leaves those words at zero counts.  No input size changes the
+ * workspace it needs.  FP4KV_EDEVICE if the array's device address cannot
  * be obtained.
  */
 int fp4kv_quantize_append_noalloc(const fp4kv_cache *c, const void *k, const void *v,
