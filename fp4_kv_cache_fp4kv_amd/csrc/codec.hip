@@ -613,8 +613,9 @@ __global__ __launch_bounds__(kThreads, 4) void prologue_kernel(RopeParams rp, Ap
       const uint32_t old_top =
           __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (old_top == (uint32_t)n_groups - 1u) {   // every group: reset, release all
+        // (nothing reads the top count again during the call, so the release
+        // need not wait for its reset)
         __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         // every group's phase flips: all phases are equal between calls
         // (zero at first, and each call flips every group of its grid, whose
         // size is fixed per device)
