@@ -200,3 +200,42 @@ def test_concurrent_one_pass_calls_on_two_streams(monkeypatch):
         bar = gc.workspace.cpu().numpy().view(np.uint32)[-33 * 64:].reshape(33, 64)
         assert not bar[:, 0].any(), bar[:, 0]
         say(f"cache {i}: a wait gave up: {bool(bar[32, 32])}")
+
+
+@pytest.mark.parametrize("shape", [
+    # (H, D, T, C, S, W, n_frames, token_stride): kept tokens per frame Tc = T / stride
+    (1, 64, 1, 1, 1, 1, 4, 1),      # one-token frames, one-frame chunks: Tc = 1
+    (5, 128, 33, 3, 1, 4, 10, 1),   # Tc = 33: a last 8-token group with one token
+    (3, 64, 26, 2, 2, 3, 9, 2),     # Tc = 13: the last group's odd half holds one token
+    (7, 128, 12, 1, 0, 3, 5, 1),    # Tc = 12: the last group half full, no sink
+    (2, 128, 66, 3, 1, 6, 11, 2),   # Tc = 33 from token stride 2, a 2-frame last chunk
+])
+def test_one_pass_edge_shapes_against_the_oracle(shape):
+    """The one-pass kernel (bf16 inputs) on shapes whose kept tokens end
+    inside an 8-token group or inside its 4-token half: cache bytes
+    bit-exact against the oracle at every step, through both entry points
+    (rope_append, then quantize_append of the same chunk, which must rewrite
+    the same bytes), with the rotated queries equal to rope_rel_frames'."""
+    from fp4_kv_cache_fp4kv_amd import api
+    from oracle.stream import OracleCache
+    from streams import compare_cache
+    H, D, T, C, S, W, n_frames, stride = shape
+    w = wl.Workload(f"edge{H}_{D}_{T}", H=H, D=D, T=T, C=C, S=S, W=W, n_frames=n_frames,
+                    seed=97 + H, dtype="bf16", outlier_p=0.01, outlier_scale=20.0,
+                    token_stride=stride)
+    gc = api.FP4KVCache(w.H, w.D, w.T, w.C, w.S, w.W, w.token_stride)
+    oc = OracleCache.for_workload(w)
+    for c in range(w.n_chunks):
+        f0, n = w.chunk_frames(c)
+        (q, qb), (k, kb), (v, vb) = step_inputs(w, c)
+        say(f"one-pass edge shape {shape} step {c} frames {f0}..{f0 + n - 1}")
+        qd, kd, vd = device_tensor(q, qb), device_tensor(k, kb), device_tensor(v, vb)
+        got = api.rope_append(gc, qd, kd, vd, f0, n, [0] * n)
+        ref = api.rope_rel_frames(gc, qd, f0, n)
+        torch.cuda.synchronize()
+        oc.append(k, v, f0, n, [0] * n)
+        assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), c
+        assert not compare_cache(gc, oc), c
+        api.quantize_append(gc, kd, vd, f0, n, [0] * n)
+        assert not compare_cache(gc, oc), c
+    _barrier_words_clear(gc)
