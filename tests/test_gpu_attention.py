@@ -306,16 +306,18 @@ def test_attention_long_stream_240_chunks():
                 heads=[0, w.H - 1], fused=True, filler=True)
 
 
-def test_attention_full_size_bf16_output_default_split():
-    """The benchmark's own launch: the 1.3B-like layer (1% outliers x20) at a
-    steady step, bf16 output with the default split over every CU.  Every
-    row of two heads: the bf16 output equals the float32 output rounded
-    once, the float32 output meets the bar, and the bf16 output meets it
-    once its own final rounding is allowed for: max-abs beyond half a bf16
-    ulp, mean-abs against the oracle rounded to bf16 (the rounding alone
-    has a mean of about 1e-3 on these outputs)."""
+@pytest.mark.parametrize("name", ["l13b", "l5b"])
+def test_attention_full_size_bf16_output_default_split(name):
+    """The benchmark's own launch: the 1.3B-like layer (1% outliers x20), and
+    the 5B-like layer (264 row blocks, cut into pieces merged in the kernel),
+    at a steady step, bf16 output with the default split over every CU.
+    Every row of two heads: the bf16 output equals the float32 output
+    rounded once, the float32 output meets the bar, and the bf16 output
+    meets it once its own final rounding is allowed for: max-abs beyond half
+    a bf16 ulp, mean-abs against the oracle rounded to bf16 (the rounding
+    alone has a mean of about 1e-3 on the 1.3B-like outputs)."""
     from fp4_kv_cache_fp4kv_amd import api
-    w = wl.L13B
+    w = wl.WORKLOADS[name]
     steady = (w.S + w.W) // w.C - 1      # the last of its 5 steps: sink + full window
     gc, oc = gpu_cache(w), OracleCache.for_workload(w)
     for c in range(steady + 1):
@@ -323,7 +325,7 @@ def test_attention_full_size_bf16_output_default_split():
         (q, qb), (k, kb), (v, vb) = step_inputs(w, c)
         shots = shots_of(w, f0, n)
         oc.append(k, v, f0, n, shots)
-        say(f"bf16-output l13b step {c}")
+        say(f"bf16-output {name} step {c}")
         qr = api.rope_append(gc, device_tensor(q, qb), device_tensor(k, kb),
                              device_tensor(v, vb), f0, n, shots)
     o16 = api.attention_chunk(gc, qr, f0, n, shots, out_dtype=torch.bfloat16)
