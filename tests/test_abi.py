@@ -64,6 +64,22 @@ def test_strerror_and_version():
     assert lib.fp4kv_append_workspace_bytes() >= 64 * 33 * 4   # re-rotation maxima
 
 
+def test_append_workspace_layout():
+    """The append workspace as the header states it: 76,288 bytes; the
+    partial maxima [2][256], the re-encoding maxima [64][256] and the 64
+    previous key scales first, then the one-pass kernel's grid barrier in
+    the last 8448 bytes (33 lines of 64 words, 256-byte aligned), whose
+    error word sits 128 bytes before the end."""
+    lib = _lib.load()
+    n = lib.fp4kv_append_workspace_bytes()
+    assert n == 76288
+    front = (2 * 256 + 64 * 256 + 64) * 4
+    barrier = 33 * 64 * 4
+    assert barrier == 8448 and front <= n - barrier and (n - barrier) % 256 == 0
+    error_word = n - barrier + (32 * 64 + 32) * 4
+    assert error_word == n - 128
+
+
 def test_attention_workspace_bytes():
     lib = _lib.load()
     counters = 4 * _lib.FP4KV_MAX_WORKGROUPS
